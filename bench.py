@@ -1,0 +1,228 @@
+#!/usr/bin/env python3
+"""Benchmark of the whole-tensor Muon optimizer step on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one pass of the whole hot path over the batch:
+- fused momentum;
+- the Frobenius norm;
+- 5 Newton-Schulz iterations (Gram, square, update);
+- the weight apply.
+The default workload is one Qwen3-32B decoder layer's seven projection
+matrices in bf16. Inputs are seeded synthetic data, resident in HBM before the
+timed region starts.
+
+Timing follows the pages' protocol of averaging many steps (Canzona analysis
+page, section 5, "Metrics"): W untimed warm-up steps, then exactly K steps
+between two device synchronisations, timed with events on the step's stream.
+Per-kernel durations come from HIP event pairs that the library records around
+every launch during the same timed region, on the same stream.
+
+It prints one JSON line, with value = algorithmic TFLOP/s of the whole step.
+Flops count only the triangles the method needs (see oracle.step_flops).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+F32_PEAK_TFLOPS = 157.3     # MI355X fp32 matrix, published
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="qwen3_32b_layer")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", default="1,2,0,3",
+                    help="matrix indices the oracle times for the CPU baseline")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run one plain torch copy of this many MiB (HBM counter scaling)")
+    return ap.parse_args()
+
+
+def nsflops(shapes, ns_steps):
+    """Algorithmic flops per step and per kernel kind (same count as the oracle's)."""
+    gram = square = update = 0
+    for r, c in shapes:
+        m, n = min(r, c), max(r, c)
+        gram += m * (m + 1) * n
+        square += m * m * (m + 1)
+        update += 2 * m * m * n
+    return {"gram": gram, "square": square, "update": update,
+            "total": ns_steps * (gram + square + update)}
+
+
+def cpu_baseline(wload, indices):
+    """The fp64 oracle, as it stands, on a bounded sample of the workload's matrices."""
+    import numpy as np
+    from matrix_optimizer_step_muon_amd import workloads as wl
+    from oracle import muon_ref as ref
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads") or 0) for p in threadpool_info()) or None
+    except Exception:
+        pass
+    mats = wl.generate(wload, indices)
+    f64 = [tuple(wl.stored_to_f64(x, wload.dtype) for x in t) for t in mats]
+    hp = wload.hparams()
+    t0 = time.perf_counter()
+    for (W, G, M) in f64:
+        ref.muon_step(W, G, M, **hp)
+    dt = time.perf_counter() - t0
+    flops = sum(ref.step_flops(*wload.shapes[i], wload.ns_steps) for i in indices)
+    shapes = [f"{wload.shapes[i][0]}x{wload.shapes[i][1]}" for i in indices]
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads or os.cpu_count(),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"fp64 numpy oracle, full step on {len(indices)} of {len(wload.shapes)} "
+                      f"matrices ({', '.join(shapes)}) of the same workload"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+              "(the Muon step of one rank needs no communication, so N ranks run N independent "
+              "copies of this benchmark)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from matrix_optimizer_step_muon_amd import muon as mu
+    from matrix_optimizer_step_muon_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    wload = wl.WORKLOADS[args.workload]
+    dt_torch = torch.bfloat16 if wload.dtype == "bf16" else torch.float32
+
+    print(f"[bench] generating {args.workload}: {len(wload.shapes)} matrices, "
+          f"{wload.numel / 1e6:.1f} M elements, {wload.dtype}", file=sys.stderr, flush=True)
+    dev = []
+    for i in range(len(wload.shapes)):
+        W, G, M = wl.generate_matrix(wload, i)
+        ts = []
+        for a in (W, G, M):
+            if wload.dtype == "bf16":
+                ts.append(torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda())
+            else:
+                ts.append(torch.from_numpy(a).cuda())
+        dev.append(ts)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    plan = mu.Plan(dev, **wload.hparams())
+    info = plan.info()
+    print(f"[bench] plan: workspace {plan.workspace_bytes() / 2**30:.2f} GiB, {info}",
+          file=sys.stderr, flush=True)
+
+    for _ in range(args.warmup):
+        plan.step(stream)
+    torch.cuda.synchronize()
+    plan.reset_timing()
+    plan.set_timing(True)
+
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        plan.step(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    plan.set_timing(False)
+    ktimes = plan.kernel_times()
+    ms_per_step = total_ms / args.steps
+    print(f"[bench] {args.steps} steps in {total_ms:.2f} ms", file=sys.stderr, flush=True)
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib * 2**20 // 4
+        src = torch.empty(n, dtype=torch.float32, device="cuda").uniform_()
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    fl = nsflops(wload.shapes, wload.ns_steps)
+    tflops = fl["total"] / (ms_per_step / 1e3) / 1e12
+    peak = BF16_PEAK_TFLOPS if wload.dtype == "bf16" else F32_PEAK_TFLOPS
+    upd_ms, upd_n = ktimes["update"]
+    upd_avg = upd_ms / max(upd_n, 1)
+    upd_tflops = fl["update"] / (upd_avg / 1e3) / 1e12 if upd_n else None
+    per_kernel = {k: {"avg_ms": round(v[0] / v[1], 4), "launches": v[1],
+                      "ms_per_step": round(v[0] / args.steps, 4)} for k, v in ktimes.items() if v[1]}
+    elem = 2 if wload.dtype == "bf16" else 4
+    mom_ms = ktimes["momentum"][0] / max(ktimes["momentum"][1], 1)
+    # Momentum kernel algorithmic bytes: read G, M; write M' and U.
+    mom_gbs = 4 * elem * wload.numel / (mom_ms / 1e3) / 1e9 if ktimes["momentum"][1] else None
+
+    out = {
+        "metric": "Muon optimizer-step ms + achieved bf16 MFMA TFLOP/s (fraction of peak) per rank share",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wload.dtype,
+        "data": "synthetic",
+        "config": {"workload": args.workload, "matrices": len(wload.shapes),
+                   "shapes": sorted({f"{r}x{c}" for r, c in wload.shapes}),
+                   "elements": wload.numel, "ns_steps": wload.ns_steps, "lr": wload.lr,
+                   "beta": wload.beta, "nesterov": wload.nesterov,
+                   "alg_tflop_per_step": round(fl["total"] / 1e12, 3)},
+        "fraction_of_peak": round(tflops / peak, 4),
+        "roofline": {
+            "kernel": "update (X' = aX + BX; weight apply on the last iteration)",
+            "bound": "mfma",
+            "achieved": round(upd_tflops, 2) if upd_tflops else None,
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(upd_tflops / peak, 4) if upd_tflops else None,
+            "traffic": None,
+            "alg_tflop_per_launch": round(fl["update"] / 1e12, 4),
+            "avg_launch_ms": round(upd_avg, 4),
+        },
+        "kernels": per_kernel,
+        "momentum_hbm": {"achieved_gbs": round(mom_gbs, 1) if mom_gbs else None,
+                         "peak_gbs": HBM_PEAK_GBS, "alg_bytes_per_elem": 4 * elem},
+        "device": torch.cuda.get_device_name(0),
+        "host": platform.node(),
+    }
+    plan.close()
+    del dev
+    torch.cuda.empty_cache()
+
+    if not args.no_cpu_baseline:
+        idx = [int(x) for x in args.cpu_sample.split(",") if x != ""]
+        print(f"[bench] cpu baseline: oracle on matrices {idx}", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(wload, idx)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

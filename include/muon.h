@@ -1,0 +1,159 @@
+/*
+ * muon.h: C ABI of the whole-tensor Muon optimizer step on one gfx950 GPU.
+ *
+ * The operation. A data-parallel rank updates the whole matrices it owns with
+ * no communication. This is the "optimizer step (local)" phase of the Canzona
+ * analysis page (paper-graph-ui), section 3.4, DP per-iteration execution. The
+ * step also equals ΔW = Muon_step(G, States_local) followed by P <- P + ΔW,
+ * from the micro-group lifecycle in the same section (steps 2 and 4). The
+ * update has the form W_{t+1} = W_t - eta * MatrixOp(W_t, grad W_t) (same page,
+ * section 2). Muon's MatrixOp orthogonalises the whole gradient with
+ * Newton-Schulz iterations, and the momentum buffer is state that stays on the
+ * owning rank (section 3.4, "Task abstraction").
+ *
+ * For every matrix (rows r, cols c) one step computes:
+ *   M' = beta*M + G                          momentum, updated in place
+ *   U  = G + beta*M'   (nesterov; else M')
+ *   X0 = U (or U^T if r > c, so X is m x n with m <= n) / (||U||_F + eps)
+ *   T times: A = X X^T;  B = b*A + c*A*A;  X = a*X + B X
+ *   O  = X (or X^T if r > c)
+ *   W' = W - lr * sqrt(max(1, r/c)) * O      weights, updated in place
+ *
+ * Conventions for every function:
+ * - It returns muon_status (0 = MUON_OK) and never throws or aborts across the
+ *   ABI. On error, muon_last_error() gives this thread's message.
+ * - Pointers named w, g, m and delta are device pointers. They address
+ *   row-major, contiguous matrices of one dtype.
+ * - Every other pointer is a host pointer.
+ */
+#ifndef MUON_H_
+#define MUON_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MUON_OK = 0,
+  MUON_ERR_INVALID_ARG = -1, /* null/negative/non-finite argument, bad shape   */
+  MUON_ERR_ALIAS = -2,       /* two device ranges of the batch overlap         */
+  MUON_ERR_ALIGN = -3,       /* a device pointer is not 16-byte aligned        */
+  MUON_ERR_UNSUPPORTED = -4, /* dtype or option not supported                  */
+  MUON_ERR_HIP = -5,         /* a HIP runtime call failed (message has it)     */
+  MUON_ERR_OOM = -6          /* workspace allocation failed                    */
+} muon_status;
+
+typedef enum {
+  MUON_F32 = 0,  /* W, G, M fp32; all arithmetic fp32 (fp32 MFMA)          */
+  MUON_BF16 = 1  /* W, G, M bf16; bf16 MFMA with fp32 accumulation,         */
+                 /* intermediates stored bf16 (round to nearest even)      */
+} muon_dtype;
+
+/* One matrix of the batch: rows x cols, row-major, contiguous.
+ * w     weights, updated in place. May be NULL when delta is set.
+ * g     gradient, read only.
+ * m     momentum buffer, updated in place.
+ * delta optional (NULL = none). When set, it receives
+ *       Delta W = -lr*sqrt(max(1,r/c))*O, the update that the host rank
+ *       returns in the micro-group lifecycle (Canzona analysis page, section
+ *       3.4, step 2).
+ * All four ranges must be 16-byte aligned and must not overlap any other
+ * range of the batch. */
+typedef struct {
+  void* w;
+  const void* g;
+  void* m;
+  void* delta;
+  int64_t rows;
+  int64_t cols;
+} muon_matrix;
+
+/* Hyperparameters. muon_hparams_default() fills in:
+ * lr = 0.02, beta = 0.95, eps = 1e-7, (a,b,c) = (3.4445, -4.7750, 2.0315),
+ * ns_steps = 5, nesterov = 1, dtype = MUON_BF16. */
+typedef struct {
+  float lr;
+  float beta;     /* momentum, 0 <= beta < 1                               */
+  float eps;      /* added to the Frobenius norm, eps >= 0                 */
+  float a, b, c;  /* Newton-Schulz polynomial a*x + b*x^3 + c*x^5          */
+  int32_t ns_steps; /* >= 0; 0 applies the normalised direction itself    */
+  int32_t nesterov; /* 0 or 1                                              */
+  int32_t dtype;    /* muon_dtype                                          */
+} muon_hparams;
+
+typedef struct muon_plan_s* muon_plan_t;
+
+/* Fills *hp with the defaults listed above. Returns INVALID_ARG if hp is NULL. */
+muon_status muon_hparams_default(muon_hparams* hp);
+
+/* Builds a static plan for a batch of n matrices. The plan is computed once
+ * and reused every step; the pages' planners likewise run once at
+ * initialisation (Canzona analysis page, section 3.3 "Output and offline
+ * nature").
+ * mats  host array of n descriptors. The plan keeps the device pointers, so
+ *       the tensors must stay allocated and unmoved until muon_plan_destroy.
+ * hp    host pointer to the hyperparameters (copied).
+ * out   receives the plan handle (NULL on error).
+ * Every argument is validated before any HIP call. Errors: INVALID_ARG (n < 1,
+ * null pointers, rows or cols < 1, non-finite lr/beta/eps/a/b/c, beta outside
+ * [0,1), eps < 0, ns_steps < 0), ALIAS, ALIGN, UNSUPPORTED (dtype). Then the
+ * plan allocates and zeroes its device workspace on the current device: HIP
+ * or OOM on failure. The call synchronises the device once, at its end. */
+muon_status muon_plan(const muon_matrix* mats, int32_t n, const muon_hparams* hp,
+                      muon_plan_t* out);
+
+/* Device workspace bytes held by the plan (written to *bytes). */
+muon_status muon_plan_workspace_bytes(muon_plan_t plan, size_t* bytes);
+
+/* Enqueues one step over the whole batch on `stream` (a hipStream_t; NULL is
+ * the null stream). It is asynchronous: no host synchronisation and no
+ * allocation. Launch errors return HIP; faults surface at the caller's next
+ * synchronisation. A plan must not be stepped concurrently on two streams,
+ * because its work-queue counters live in its workspace. Matrices are
+ * independent, and the result does not depend on descriptor order. For a
+ * fixed plan the result is bitwise deterministic. */
+muon_status muon_step(muon_plan_t plan, void* stream);
+
+/* Frees the plan and its workspace. NULL is a no-op. Synchronises the device. */
+muon_status muon_plan_destroy(muon_plan_t plan);
+
+/* This thread's last error message ("" if none). Valid until this thread's
+ * next call into the library. */
+const char* muon_last_error(void);
+
+/* Kernel kinds, for the timing counters below. */
+typedef enum {
+  MUON_K_MOMENTUM = 0, /* fused momentum + Nesterov + sum-of-squares partials */
+  MUON_K_NORM = 1,     /* fixed-order norm reduction to 1/(||U||+eps)        */
+  MUON_K_GRAM = 2,     /* symmetric A = X X^T (upper tiles, mirrored)        */
+  MUON_K_SQUARE = 3,   /* B = b*A + c*A*A (upper tiles, mirrored)            */
+  MUON_K_UPDATE = 4,   /* X = a*X + B X; on the last step, the weight apply  */
+  MUON_K_APPLY = 5,    /* weight apply when ns_steps == 0                    */
+  MUON_K_COUNT = 6
+} muon_kernel_kind;
+
+/* enable != 0: every later muon_step records a HIP event pair on its stream
+ * around each kernel launch. Timing is off by default. */
+muon_status muon_plan_set_timing(muon_plan_t plan, int32_t enable);
+
+/* Waits for the recorded events and adds their durations to per-kind totals.
+ * Then writes, for kind k in [0, MUON_K_COUNT):
+ *   total_ms[k] = summed launch durations;
+ *   launches[k] = number of launches.
+ * Either array may be NULL. Totals accumulate until muon_plan_reset_timing. */
+muon_status muon_plan_kernel_times(muon_plan_t plan, double* total_ms, int64_t* launches);
+muon_status muon_plan_reset_timing(muon_plan_t plan);
+
+/* Plan facts, for logs and benchmarks (host pointers; any may be NULL):
+ * n_tiles[k] = tiles per launch of kind k (K1 tiles for MOMENTUM);
+ * grid[k]    = workgroups launched per launch of kind k. */
+muon_status muon_plan_info(muon_plan_t plan, int64_t* n_tiles, int64_t* grid);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MUON_H_ */

@@ -1,0 +1,415 @@
+// C ABI of the whole-tensor Muon step (include/muon.h): validation, the
+// static plan (orientation, padding, LPT tile tables, workspace layout) and
+// the per-step launch sequence.
+//
+// The plan is computed once and reused every step, as the pages' planners are
+// (Canzona analysis page, section 3.3, "Output and offline nature"). Each
+// GEMM phase's tile list is sorted by cost, longest first. This is the pages'
+// LPT rule (section 3.4, "Why LPT ordering matters"), with the cost of a tile
+// taken as its exact multiply-add count. The pages also weigh a FLOPs-based cost
+// against numel (section 5, Figure 16).
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "muon.h"
+#include "muon_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+muon_status fail(muon_status st, const std::string& msg) {
+  g_last_error = msg;
+  return st;
+}
+
+muon_status hip_fail(hipError_t e, const char* what) {
+  return fail(MUON_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+constexpr int64_t kMaxDim = int64_t(1) << 24;  // tile indices are packed in 16 bits
+constexpr int32_t kMaxNsSteps = 1000;
+
+}  // namespace
+
+struct muon_plan_s {
+  muon_hparams hp{};
+  int dtype = 1;
+  int elem = 2;
+  int n = 0;
+  int device = 0;
+  int tile = muon::kTileBF16;
+
+  std::vector<muon::MatDev> mats;  // host copy (device pointers inside)
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+
+  muon::MatDev* d_mats = nullptr;
+  int32_t* d_prefix = nullptr;
+  float* d_partials = nullptr;
+  float* d_scale = nullptr;
+  int32_t* d_counters = nullptr;
+  int32_t n_counters = 0;
+  muon::Tile* d_tiles[3] = {nullptr, nullptr, nullptr};
+  int32_t n_tiles[3] = {0, 0, 0};
+  int32_t grid[3] = {0, 0, 0};
+  int32_t ew_blocks = 0;
+
+  bool timing = false;
+  struct Rec { int kind; hipEvent_t start, end; };
+  std::vector<Rec> pending;
+  std::vector<hipEvent_t> pool;
+  double total_ms[MUON_K_COUNT] = {};
+  int64_t launches[MUON_K_COUNT] = {};
+};
+
+extern "C" {
+
+const char* muon_last_error(void) { return g_last_error.c_str(); }
+
+muon_status muon_hparams_default(muon_hparams* hp) {
+  if (!hp) return fail(MUON_ERR_INVALID_ARG, "hp is NULL");
+  hp->lr = 0.02f;
+  hp->beta = 0.95f;
+  hp->eps = 1e-7f;
+  hp->a = 3.4445f;
+  hp->b = -4.7750f;
+  hp->c = 2.0315f;
+  hp->ns_steps = 5;
+  hp->nesterov = 1;
+  hp->dtype = MUON_BF16;
+  return MUON_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+muon_status validate(const muon_matrix* mats, int32_t n, const muon_hparams* hp) {
+  if (!mats) return fail(MUON_ERR_INVALID_ARG, "mats is NULL");
+  if (n < 1) return fail(MUON_ERR_INVALID_ARG, "n must be >= 1");
+  if (!hp) return fail(MUON_ERR_INVALID_ARG, "hp is NULL");
+  const float fs[6] = {hp->lr, hp->beta, hp->eps, hp->a, hp->b, hp->c};
+  const char* names[6] = {"lr", "beta", "eps", "a", "b", "c"};
+  for (int i = 0; i < 6; ++i)
+    if (!std::isfinite(fs[i])) return fail(MUON_ERR_INVALID_ARG, std::string(names[i]) + " is not finite");
+  if (!(hp->beta >= 0.f && hp->beta < 1.f)) return fail(MUON_ERR_INVALID_ARG, "beta must be in [0, 1)");
+  if (hp->eps < 0.f) return fail(MUON_ERR_INVALID_ARG, "eps must be >= 0");
+  if (hp->ns_steps < 0 || hp->ns_steps > kMaxNsSteps)
+    return fail(MUON_ERR_INVALID_ARG, "ns_steps must be in [0, 1000]");
+  if (hp->nesterov != 0 && hp->nesterov != 1) return fail(MUON_ERR_INVALID_ARG, "nesterov must be 0 or 1");
+  if (hp->dtype != MUON_F32 && hp->dtype != MUON_BF16)
+    return fail(MUON_ERR_UNSUPPORTED, "dtype must be MUON_F32 or MUON_BF16");
+  const size_t elem = hp->dtype == MUON_BF16 ? 2 : 4;
+
+  struct Range { uintptr_t lo, hi; int mat; const char* what; };
+  std::vector<Range> ranges;
+  ranges.reserve(size_t(n) * 4);
+  for (int32_t i = 0; i < n; ++i) {
+    const muon_matrix& d = mats[i];
+    const std::string at = "matrix " + std::to_string(i) + ": ";
+    if (d.rows < 1 || d.cols < 1) return fail(MUON_ERR_INVALID_ARG, at + "rows and cols must be >= 1");
+    if (d.rows > kMaxDim || d.cols > kMaxDim)
+      return fail(MUON_ERR_INVALID_ARG, at + "rows and cols must be <= 2^24");
+    if (!d.g) return fail(MUON_ERR_INVALID_ARG, at + "g is NULL");
+    if (!d.m) return fail(MUON_ERR_INVALID_ARG, at + "m is NULL");
+    if (!d.w && !d.delta) return fail(MUON_ERR_INVALID_ARG, at + "w and delta are both NULL");
+    const uintptr_t bytes = uintptr_t(d.rows) * uintptr_t(d.cols) * elem;
+    const void* ptrs[4] = {d.w, d.g, d.m, d.delta};
+    const char* what[4] = {"w", "g", "m", "delta"};
+    for (int k = 0; k < 4; ++k) {
+      if (!ptrs[k]) continue;
+      const uintptr_t p = reinterpret_cast<uintptr_t>(ptrs[k]);
+      if (p % 16 != 0) return fail(MUON_ERR_ALIGN, at + what[k] + " is not 16-byte aligned");
+      ranges.push_back({p, p + bytes, i, what[k]});
+    }
+  }
+  std::sort(ranges.begin(), ranges.end(), [](const Range& x, const Range& y) { return x.lo < y.lo; });
+  for (size_t k = 1; k < ranges.size(); ++k)
+    if (ranges[k].lo < ranges[k - 1].hi)
+      return fail(MUON_ERR_ALIAS, "matrix " + std::to_string(ranges[k - 1].mat) + " " + ranges[k - 1].what +
+                                      " overlaps matrix " + std::to_string(ranges[k].mat) + " " +
+                                      ranges[k].what);
+  return MUON_OK;
+}
+
+void free_plan(muon_plan_s* p) {
+  if (!p) return;
+  if (p->ws) (void)hipFree(p->ws);
+  for (auto& r : p->pending) { (void)hipEventDestroy(r.start); (void)hipEventDestroy(r.end); }
+  for (auto e : p->pool) (void)hipEventDestroy(e);
+  delete p;
+}
+
+}  // namespace
+
+extern "C" {
+
+muon_status muon_plan(const muon_matrix* mats, int32_t n, const muon_hparams* hp, muon_plan_t* out) {
+  if (!out) return fail(MUON_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  muon_status st = validate(mats, n, hp);
+  if (st != MUON_OK) return st;
+
+  auto* p = new muon_plan_s();
+  p->hp = *hp;
+  p->dtype = hp->dtype;
+  p->elem = hp->dtype == MUON_BF16 ? 2 : 4;
+  p->n = n;
+  p->tile = hp->dtype == MUON_BF16 ? muon::kTileBF16 : muon::kTileF32;
+  const int64_t T = p->tile;
+
+  // Orientation, padding and workspace offsets.
+  p->mats.resize(n);
+  std::vector<size_t> off(n * 6);
+  size_t cursor = 0;
+  auto take = [&](size_t bytes) { size_t o = cursor; cursor = round_up(cursor + bytes, 256); return o; };
+  std::vector<int32_t> prefix(n + 1, 0);
+  int32_t parts = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const muon_matrix& s = mats[i];
+    muon::MatDev& d = p->mats[i];
+    std::memset(&d, 0, sizeof(d));
+    d.rows = int32_t(s.rows);
+    d.cols = int32_t(s.cols);
+    d.tall = s.rows > s.cols;
+    d.m = int32_t(std::min(s.rows, s.cols));
+    d.n = int32_t(std::max(s.rows, s.cols));
+    d.mp = int32_t(round_up(d.m, T));
+    d.np = int32_t(round_up(d.n, T));
+    d.ew_tiles_c = int32_t((s.cols + muon::kEwTile - 1) / muon::kEwTile);
+    const int32_t tr = int32_t((s.rows + muon::kEwTile - 1) / muon::kEwTile);
+    d.n_parts = tr * d.ew_tiles_c;
+    d.part_off = parts;
+    parts += d.n_parts;
+    prefix[i + 1] = prefix[i] + d.n_parts;
+    d.lr_scale = float(double(hp->lr) * std::sqrt(std::max(1.0, double(s.rows) / double(s.cols))));
+    d.w = s.w;
+    d.delta = s.delta;
+    d.g = s.g;
+    d.mom = s.m;
+    const size_t xbytes = size_t(d.mp) * d.np * p->elem;
+    const size_t abytes = size_t(d.mp) * d.mp * p->elem;
+    off[i * 6 + 0] = take(xbytes);
+    off[i * 6 + 1] = take(xbytes);
+    off[i * 6 + 2] = take(xbytes);
+    off[i * 6 + 3] = take(xbytes);
+    off[i * 6 + 4] = take(abytes);
+    off[i * 6 + 5] = take(abytes);
+  }
+  p->ew_blocks = prefix[n];
+  const size_t o_mats = take(sizeof(muon::MatDev) * n);
+  const size_t o_prefix = take(sizeof(int32_t) * (n + 1));
+  const size_t o_parts = take(sizeof(float) * std::max(parts, 1));
+  const size_t o_scale = take(sizeof(float) * n);
+  p->n_counters = std::max(3 * hp->ns_steps, 1);
+  const size_t o_ctr = take(sizeof(int32_t) * p->n_counters);
+
+  // Tile tables, each sorted longest first. Every tile of a phase has the
+  // same area, so the cost is the contraction length K. Ties keep
+  // (matrix, tile row, tile col) order.
+  struct HT { int64_t cost; int32_t mat, ti, tj; };
+  std::vector<HT> tl[3];
+  for (int32_t i = 0; i < n; ++i) {
+    const muon::MatDev& d = p->mats[i];
+    const int32_t tm = d.mp / T, tn = d.np / T;
+    for (int32_t a = 0; a < tm; ++a)
+      for (int32_t b = a; b < tm; ++b) {
+        tl[muon::kGram].push_back({d.np, i, a, b});
+        tl[muon::kSquare].push_back({d.mp, i, a, b});
+      }
+    for (int32_t a = 0; a < tm; ++a)
+      for (int32_t b = 0; b < tn; ++b) tl[muon::kUpdate].push_back({d.mp, i, a, b});
+  }
+  size_t o_tiles[3];
+  std::vector<muon::Tile> tiles[3];
+  for (int ph = 0; ph < 3; ++ph) {
+    std::stable_sort(tl[ph].begin(), tl[ph].end(), [](const HT& x, const HT& y) { return x.cost > y.cost; });
+    tiles[ph].reserve(tl[ph].size());
+    for (const HT& h : tl[ph]) tiles[ph].push_back({h.mat, (h.ti << 16) | h.tj});
+    p->n_tiles[ph] = int32_t(tiles[ph].size());
+    o_tiles[ph] = take(sizeof(muon::Tile) * std::max<size_t>(tiles[ph].size(), 1));
+  }
+  p->ws_bytes = cursor;
+
+  // ---- HIP from here on.
+  hipError_t e = hipGetDevice(&p->device);
+  if (e != hipSuccess) { free_plan(p); return hip_fail(e, "hipGetDevice"); }
+  int n_cu = 0;
+  e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, p->device);
+  if (e != hipSuccess) { free_plan(p); return hip_fail(e, "hipDeviceGetAttribute"); }
+  const int32_t resident = n_cu * muon::gemm_blocks_per_cu(p->dtype);
+  for (int ph = 0; ph < 3; ++ph) p->grid[ph] = std::max(1, std::min(p->n_tiles[ph], resident));
+
+  e = hipMalloc(&p->ws, p->ws_bytes);
+  if (e != hipSuccess) {
+    p->ws = nullptr;
+    free_plan(p);
+    (void)hipGetLastError();
+    return fail(MUON_ERR_OOM, "hipMalloc of " + std::to_string(p->ws_bytes) + " workspace bytes failed");
+  }
+  char* base = static_cast<char*>(p->ws);
+  e = hipMemset(p->ws, 0, p->ws_bytes);
+  if (e != hipSuccess) { free_plan(p); return hip_fail(e, "hipMemset"); }
+  for (int32_t i = 0; i < n; ++i) {
+    muon::MatDev& d = p->mats[i];
+    d.x[0] = base + off[i * 6 + 0];
+    d.x[1] = base + off[i * 6 + 1];
+    d.xt[0] = base + off[i * 6 + 2];
+    d.xt[1] = base + off[i * 6 + 3];
+    d.a = base + off[i * 6 + 4];
+    d.b = base + off[i * 6 + 5];
+  }
+  p->d_mats = reinterpret_cast<muon::MatDev*>(base + o_mats);
+  p->d_prefix = reinterpret_cast<int32_t*>(base + o_prefix);
+  p->d_partials = reinterpret_cast<float*>(base + o_parts);
+  p->d_scale = reinterpret_cast<float*>(base + o_scale);
+  p->d_counters = reinterpret_cast<int32_t*>(base + o_ctr);
+  for (int ph = 0; ph < 3; ++ph) p->d_tiles[ph] = reinterpret_cast<muon::Tile*>(base + o_tiles[ph]);
+
+  struct Up { void* dst; const void* src; size_t bytes; };
+  const Up ups[5] = {
+      {p->d_mats, p->mats.data(), sizeof(muon::MatDev) * n},
+      {p->d_prefix, prefix.data(), sizeof(int32_t) * (n + 1)},
+      {p->d_tiles[0], tiles[0].data(), sizeof(muon::Tile) * tiles[0].size()},
+      {p->d_tiles[1], tiles[1].data(), sizeof(muon::Tile) * tiles[1].size()},
+      {p->d_tiles[2], tiles[2].data(), sizeof(muon::Tile) * tiles[2].size()},
+  };
+  for (const Up& u : ups) {
+    if (u.bytes == 0) continue;
+    e = hipMemcpy(u.dst, u.src, u.bytes, hipMemcpyHostToDevice);
+    if (e != hipSuccess) { free_plan(p); return hip_fail(e, "hipMemcpy"); }
+  }
+  e = hipDeviceSynchronize();
+  if (e != hipSuccess) { free_plan(p); return hip_fail(e, "hipDeviceSynchronize"); }
+  *out = p;
+  return MUON_OK;
+}
+
+muon_status muon_plan_workspace_bytes(muon_plan_t p, size_t* bytes) {
+  if (!p || !bytes) return fail(MUON_ERR_INVALID_ARG, "NULL argument");
+  *bytes = p->ws_bytes;
+  return MUON_OK;
+}
+
+muon_status muon_plan_info(muon_plan_t p, int64_t* n_tiles, int64_t* grid) {
+  if (!p) return fail(MUON_ERR_INVALID_ARG, "plan is NULL");
+  for (int k = 0; k < MUON_K_COUNT; ++k) {
+    int64_t t = 0, g = 0;
+    if (k == MUON_K_MOMENTUM || k == MUON_K_APPLY) { t = p->ew_blocks; g = p->ew_blocks; }
+    else if (k == MUON_K_NORM) { t = p->n; g = p->n; }
+    else { t = p->n_tiles[k - MUON_K_GRAM]; g = p->grid[k - MUON_K_GRAM]; }
+    if (n_tiles) n_tiles[k] = t;
+    if (grid) grid[k] = g;
+  }
+  return MUON_OK;
+}
+
+muon_status muon_plan_set_timing(muon_plan_t p, int32_t enable) {
+  if (!p) return fail(MUON_ERR_INVALID_ARG, "plan is NULL");
+  p->timing = enable != 0;
+  return MUON_OK;
+}
+
+muon_status muon_plan_reset_timing(muon_plan_t p) {
+  if (!p) return fail(MUON_ERR_INVALID_ARG, "plan is NULL");
+  muon_status st = muon_plan_kernel_times(p, nullptr, nullptr);
+  for (int k = 0; k < MUON_K_COUNT; ++k) { p->total_ms[k] = 0; p->launches[k] = 0; }
+  return st;
+}
+
+muon_status muon_plan_kernel_times(muon_plan_t p, double* total_ms, int64_t* launches) {
+  if (!p) return fail(MUON_ERR_INVALID_ARG, "plan is NULL");
+  muon_status st = MUON_OK;
+  for (auto& r : p->pending) {
+    float ms = 0.f;
+    hipError_t e = hipEventSynchronize(r.end);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.start, r.end);
+    if (e != hipSuccess && st == MUON_OK) st = hip_fail(e, "hipEventElapsedTime");
+    p->total_ms[r.kind] += ms;
+    p->launches[r.kind] += 1;
+    p->pool.push_back(r.start);
+    p->pool.push_back(r.end);
+  }
+  p->pending.clear();
+  for (int k = 0; k < MUON_K_COUNT; ++k) {
+    if (total_ms) total_ms[k] = p->total_ms[k];
+    if (launches) launches[k] = p->launches[k];
+  }
+  return st;
+}
+
+muon_status muon_step(muon_plan_t p, void* stream) {
+  if (!p) return fail(MUON_ERR_INVALID_ARG, "plan is NULL");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (cur != p->device) {
+    e = hipSetDevice(p->device);
+    if (e != hipSuccess) return hip_fail(e, "hipSetDevice");
+  }
+
+  auto ev = [&](hipEvent_t* out) -> hipError_t {
+    if (!p->pool.empty()) { *out = p->pool.back(); p->pool.pop_back(); return hipSuccess; }
+    return hipEventCreate(out);
+  };
+  muon_status st = MUON_OK;
+  auto run = [&](int kind, auto&& launch) {
+    if (st != MUON_OK) return;
+    hipEvent_t a = nullptr, b = nullptr;
+    if (p->timing) {
+      hipError_t r = ev(&a);
+      if (r == hipSuccess) r = ev(&b);
+      if (r == hipSuccess) r = hipEventRecord(a, s);
+      if (r != hipSuccess) { st = hip_fail(r, "timing event"); return; }
+    }
+    hipError_t r = launch();
+    if (r != hipSuccess) { st = hip_fail(r, "kernel launch"); return; }
+    if (p->timing) {
+      r = hipEventRecord(b, s);
+      if (r != hipSuccess) { st = hip_fail(r, "hipEventRecord"); return; }
+      p->pending.push_back({kind, a, b});
+    }
+  };
+
+  muon::StepCoeffs co{p->hp.a, p->hp.b, p->hp.c, p->hp.beta, p->hp.eps, p->hp.nesterov};
+  muon::EwArgs ew{p->d_mats, p->d_prefix, p->n, p->d_partials, p->d_counters, p->n_counters, p->d_scale, co};
+  run(MUON_K_MOMENTUM, [&] { return muon::launch_momentum(p->dtype, ew, p->ew_blocks, s); });
+  run(MUON_K_NORM, [&] { return muon::launch_norm(p->d_mats, p->d_partials, p->d_scale, p->n, p->hp.eps, s); });
+  const int T = p->hp.ns_steps;
+  if (T == 0) {
+    run(MUON_K_APPLY, [&] { return muon::launch_apply(p->dtype, ew, p->ew_blocks, s); });
+  }
+  for (int it = 0; it < T; ++it) {
+    for (int ph = 0; ph < 3; ++ph) {
+      muon::PhaseArgs a{p->d_mats, p->d_tiles[ph], p->n_tiles[ph], p->d_counters + 3 * it + ph, p->d_scale,
+                        it & 1, it == 0, it == T - 1, co};
+      run(MUON_K_GRAM + ph,
+          [&] { return muon::launch_phase(p->dtype, muon::Phase(ph), a, p->grid[ph], s); });
+    }
+  }
+  if (cur != p->device) (void)hipSetDevice(cur);
+  return st;
+}
+
+muon_status muon_plan_destroy(muon_plan_t p) {
+  if (!p) return MUON_OK;
+  hipError_t e = hipDeviceSynchronize();
+  free_plan(p);
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+  return MUON_OK;
+}
+
+}  // extern "C"

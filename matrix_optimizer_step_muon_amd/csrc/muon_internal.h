@@ -1,0 +1,88 @@
+// Internal types shared by the host planner (muon_api.cpp) and the gfx950
+// kernels (muon_kernels.hip). Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace muon {
+
+// Tile geometry of the two GEMM engines. Workspace matrices are padded to a
+// multiple of the tile edge. Padding is zero and stays zero, because every
+// epilogue writes 0 outside the valid region.
+constexpr int kTileBF16 = 256;  // bf16 engine: 256 x 256 output tiles, K step 64
+constexpr int kTileF32 = 128;   // fp32 engine: 128 x 128 output tiles, K step 32
+constexpr int kEwTile = 64;     // elementwise kernels: 64 x 64 tiles
+
+// One matrix of the batch as the kernels see it. X is the m x n orientation
+// of U (m = min(rows, cols)): U itself, or U^T when rows > cols.
+struct MatDev {
+  void* x[2];         // X ping/pong: mp x np, row-major, ld = np
+  void* xt[2];        // X^T ping/pong: np x mp, row-major, ld = mp
+  void* a;            // A = X X^T: mp x mp
+  void* b;            // B = b*A + c*A*A: mp x mp
+  void* w;            // weights rows x cols (may be null)
+  void* delta;        // Delta W rows x cols (may be null)
+  const void* g;      // gradient rows x cols
+  void* mom;          // momentum rows x cols
+  int32_t rows, cols;
+  int32_t m, n;       // m = min(rows, cols), n = max(rows, cols)
+  int32_t mp, np;     // m, n rounded up to the GEMM tile edge
+  int32_t tall;       // rows > cols
+  int32_t ew_tiles_c; // elementwise tiles along cols: ceil(cols / 64)
+  int32_t part_off;   // first norm-partial slot of this matrix
+  int32_t n_parts;    // number of elementwise tiles (= partial slots)
+  float lr_scale;     // lr * sqrt(max(1, rows / cols))
+  float pad_;
+};
+
+// One output tile of a GEMM phase: matrix index and tile coordinates.
+struct Tile {
+  int32_t mat;
+  int32_t ij;  // (ti << 16) | tj
+};
+
+struct StepCoeffs {
+  float a, b, c;  // Newton-Schulz polynomial
+  float beta;     // momentum
+  float eps;      // norm guard
+  int32_t nesterov;
+};
+
+enum Phase { kGram = 0, kSquare = 1, kUpdate = 2 };
+
+// Arguments of one persistent GEMM-phase launch.
+struct PhaseArgs {
+  const MatDev* mats;
+  const Tile* tiles;   // LPT-ordered tile list of this phase
+  int32_t n_tiles;
+  int32_t* counter;    // work-queue head of this launch (zeroed by the momentum kernel)
+  const float* scale;  // per-matrix 1/(||U||_F + eps)
+  int32_t src;         // ping/pong index read this iteration
+  int32_t first;       // first iteration: fold the norm scale in
+  int32_t last;        // last iteration: apply to W / delta instead of storing X
+  StepCoeffs co;
+};
+
+struct EwArgs {
+  const MatDev* mats;
+  const int32_t* prefix;  // prefix[i] = first elementwise tile of matrix i; prefix[n] = total
+  int32_t n_mats;
+  float* partials;        // one fp32 sum of squares per elementwise tile
+  int32_t* counters;      // zeroed by the momentum kernel
+  int32_t n_counters;
+  const float* scale;
+  StepCoeffs co;
+};
+
+// Launchers (muon_kernels.hip). dtype: 0 = fp32, 1 = bf16.
+hipError_t launch_momentum(int dtype, const EwArgs& args, int32_t n_blocks, hipStream_t s);
+hipError_t launch_norm(const MatDev* mats, const float* partials, float* scale, int32_t n_mats,
+                       float eps, hipStream_t s);
+hipError_t launch_apply(int dtype, const EwArgs& args, int32_t n_blocks, hipStream_t s);
+hipError_t launch_phase(int dtype, Phase ph, const PhaseArgs& args, int32_t grid, hipStream_t s);
+
+// Workgroups per CU that the persistent GEMM kernels can keep resident.
+int gemm_blocks_per_cu(int dtype);
+
+}  // namespace muon

@@ -1,0 +1,598 @@
+// gfx950 (CDNA4) kernels of the whole-tensor Muon step.
+//
+// Kernels in one step, in launch order:
+//   momentum  fused M' = beta*M + G, U = G + beta*M' (Nesterov), U stored in
+//             both orientations, per-tile sums of squares (HBM-bound)
+//   norm      fixed-order reduction of those sums to s = 1/(||U||_F + eps)
+//   T times:
+//     gram    A = X X^T          symmetric: upper tiles only, each mirrored
+//     square  B = b*A + c*A*A    A symmetric, so A*A is too: upper tiles, mirrored
+//     update  X' = a*X + B X     on the last iteration, W -= lr*scale*O instead
+//   apply     W -= lr*scale*s*U  only when T = 0
+//
+// Muon orthogonalises the whole matrix with Newton-Schulz iterations (Canzona
+// analysis page, section 2). Those are the repeated products that mix every row
+// and column of the gradient (section 3.4, the Atomicity Constraint). The three
+// GEMM phases are dense contractions and run on MFMA:
+// - bf16 path: v_mfma_f32_32x32x16_bf16, fp32 accumulation;
+// - fp32 path: v_mfma_f32_32x32x2f32.
+// Each phase is one persistent launch over the tiles of every matrix in the
+// batch. Workgroups pull tiles from an atomic queue whose order is longest
+// first: the LPT rule the pages use to assign work to ranks (section 3.4,
+// "Why LPT ordering matters"), applied here across CUs.
+//
+// Both operands of every contraction are read along contiguous rows:
+// - X X^T: rows of X.
+// - A*A = A A^T: rows of A, since A is symmetric.
+// - B X: rows of B (symmetric) and rows of X^T, kept as a second copy.
+// So every GEMM is "NT", and each MFMA operand is a 16-byte LDS read.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "muon_internal.h"
+
+namespace muon {
+
+typedef uint16_t u16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// ------------------------------------------------------------ element access
+
+__device__ __forceinline__ float bf16_to_f32(u16 v) { return __uint_as_float((uint32_t)v << 16); }
+
+// Round to nearest even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ u16 f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u16)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (u16)(u >> 16);
+}
+
+template <class T> struct Elem;
+template <> struct Elem<float> {
+  static __device__ __forceinline__ float load(const float* p) { return *p; }
+  static __device__ __forceinline__ void store(float* p, float v) { *p = v; }
+  static __device__ __forceinline__ float round(float v) { return v; }
+};
+template <> struct Elem<u16> {
+  static __device__ __forceinline__ float load(const u16* p) { return bf16_to_f32(*p); }
+  static __device__ __forceinline__ void store(u16* p, float v) { *p = f32_to_bf16(v); }
+  static __device__ __forceinline__ float round(float v) { return bf16_to_f32(f32_to_bf16(v)); }
+};
+
+// Four consecutive elements, as one 8-byte (bf16) or 16-byte (fp32) access.
+template <class T> struct Vec4;
+template <> struct Vec4<float> {
+  static __device__ __forceinline__ void load(const float* p, float v[4]) {
+    float4 t = *reinterpret_cast<const float4*>(p);
+    v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+  }
+  static __device__ __forceinline__ void store(float* p, const float v[4]) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+};
+template <> struct Vec4<u16> {
+  static __device__ __forceinline__ void load(const u16* p, float v[4]) {
+    uint2 t = *reinterpret_cast<const uint2*>(p);
+    v[0] = __uint_as_float(t.x << 16); v[1] = __uint_as_float(t.x & 0xffff0000u);
+    v[2] = __uint_as_float(t.y << 16); v[3] = __uint_as_float(t.y & 0xffff0000u);
+  }
+  static __device__ __forceinline__ void store(u16* p, const float v[4]) {
+    uint2 t;
+    t.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+    t.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+    *reinterpret_cast<uint2*>(p) = t;
+  }
+};
+
+// ------------------------------------------------------------ GEMM engines
+//
+// Each engine computes one BM x BN output tile, C[i][j] = sum_k P[i][k] Q[j][k]
+// (P, Q row-major, K a multiple of BK), and leaves it in MFMA accumulators.
+// Accumulator layout of a 32 x 32 MFMA block, element r of lane l:
+//   column = l % 32,  row = 8*(r/4) + 4*(l/32) + r%4.
+
+struct EngineBF16 {
+  typedef u16 T;
+  static constexpr int BM = 256, BN = 256, BK = 64, NT = 512;
+  static constexpr int WM = 128, WN = 64;    // wave tile: 8 waves as 2 x 4
+  static constexpr int FM = WM / 32, FN = WN / 32;
+  static constexpr int LDS_STRIDE = BK + 8;  // u16; 144-byte rows avoid bank conflicts
+  static constexpr int STAGE = (BM + BN) * LDS_STRIDE;
+  static constexpr int LDS_BYTES = 2 * STAGE * 2;
+  static __device__ __forceinline__ int wave_m(int w) { return w >> 2; }
+  static __device__ __forceinline__ int wave_n(int w) { return w & 3; }
+
+  static __device__ __forceinline__ void run(const u16* __restrict__ P, int64_t ldp,
+                                             const u16* __restrict__ Q, int64_t ldq, int K,
+                                             u16* smem, f32x16 (&acc)[FM][FN]) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave_m(wave), wn = wave_n(wave);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    // Global -> register staging: each operand tile is BM rows x 128 bytes;
+    // a thread moves 4 16-byte chunks of each, 8 threads per row (coalesced).
+    uint4 rp[4], rq[4];
+    auto gload = [&](int k0) {
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int q = tid + p * NT, row = q >> 3, ch = q & 7;
+        rp[p] = *reinterpret_cast<const uint4*>(P + row * ldp + k0 + ch * 8);
+        rq[p] = *reinterpret_cast<const uint4*>(Q + row * ldq + k0 + ch * 8);
+      }
+    };
+    auto sstore = [&](int s) {
+      u16* sp = smem + s * STAGE;
+      u16* sq = sp + BM * LDS_STRIDE;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int q = tid + p * NT, row = q >> 3, ch = q & 7;
+        *reinterpret_cast<uint4*>(sp + row * LDS_STRIDE + ch * 8) = rp[p];
+        *reinterpret_cast<uint4*>(sq + row * LDS_STRIDE + ch * 8) = rq[p];
+      }
+    };
+
+    const int KT = K / BK;
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    for (int kt = 0; kt < KT; ++kt) {
+      const int s = kt & 1;
+      if (kt + 1 < KT) gload((kt + 1) * BK);
+      const u16* sp = smem + s * STAGE + (wm * WM + (lane & 31)) * LDS_STRIDE + (lane >> 5) * 8;
+      const u16* sq = smem + s * STAGE + BM * LDS_STRIDE + (wn * WN + (lane & 31)) * LDS_STRIDE +
+                      (lane >> 5) * 8;
+#pragma unroll
+      for (int kk = 0; kk < BK / 16; ++kk) {
+        bf16x8 fp[FM], fq[FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+          fp[i] = *reinterpret_cast<const bf16x8*>(sp + i * 32 * LDS_STRIDE + kk * 16);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          fq[j] = *reinterpret_cast<const bf16x8*>(sq + j * 32 * LDS_STRIDE + kk * 16);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp[i], fq[j], acc[i][j], 0, 0, 0);
+      }
+      // One barrier per K step: stage s^1 was last read in step kt-1, which
+      // ended with a barrier, so writing it now is safe.
+      if (kt + 1 < KT) sstore(s ^ 1);
+      __syncthreads();
+    }
+  }
+};
+
+struct EngineF32 {
+  typedef float T;
+  static constexpr int BM = 128, BN = 128, BK = 32, NT = 256;
+  static constexpr int WM = 64, WN = 64;     // wave tile: 4 waves as 2 x 2
+  static constexpr int FM = WM / 32, FN = WN / 32;
+  static constexpr int LDS_STRIDE = BK + 1;  // floats; odd stride spreads rows over banks
+  static constexpr int STAGE = (BM + BN) * LDS_STRIDE;
+  static constexpr int LDS_BYTES = 2 * STAGE * 4;
+  static __device__ __forceinline__ int wave_m(int w) { return w >> 1; }
+  static __device__ __forceinline__ int wave_n(int w) { return w & 1; }
+
+  static __device__ __forceinline__ void run(const float* __restrict__ P, int64_t ldp,
+                                             const float* __restrict__ Q, int64_t ldq, int K,
+                                             float* smem, f32x16 (&acc)[FM][FN]) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave_m(wave), wn = wave_n(wave);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    float4 rp[4], rq[4];
+    auto gload = [&](int k0) {
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int q = tid + p * NT, row = q >> 3, ch = q & 7;
+        rp[p] = *reinterpret_cast<const float4*>(P + row * ldp + k0 + ch * 4);
+        rq[p] = *reinterpret_cast<const float4*>(Q + row * ldq + k0 + ch * 4);
+      }
+    };
+    auto sstore = [&](int s) {
+      float* sp = smem + s * STAGE;
+      float* sq = sp + BM * LDS_STRIDE;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int q = tid + p * NT, row = q >> 3, ch = q & 7;
+        float* dp = sp + row * LDS_STRIDE + ch * 4;
+        float* dq = sq + row * LDS_STRIDE + ch * 4;
+        dp[0] = rp[p].x; dp[1] = rp[p].y; dp[2] = rp[p].z; dp[3] = rp[p].w;
+        dq[0] = rq[p].x; dq[1] = rq[p].y; dq[2] = rq[p].z; dq[3] = rq[p].w;
+      }
+    };
+
+    const int KT = K / BK;
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    for (int kt = 0; kt < KT; ++kt) {
+      const int s = kt & 1;
+      if (kt + 1 < KT) gload((kt + 1) * BK);
+      const float* sp = smem + s * STAGE + (wm * WM + (lane & 31)) * LDS_STRIDE + (lane >> 5);
+      const float* sq = smem + s * STAGE + BM * LDS_STRIDE + (wn * WN + (lane & 31)) * LDS_STRIDE +
+                        (lane >> 5);
+#pragma unroll
+      for (int kk = 0; kk < BK / 2; ++kk) {
+        float fp[FM], fq[FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) fp[i] = sp[i * 32 * LDS_STRIDE + kk * 2];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) fq[j] = sq[j * 32 * LDS_STRIDE + kk * 2];
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fp[i], fq[j], acc[i][j], 0, 0, 0);
+      }
+      if (kt + 1 < KT) sstore(s ^ 1);
+      __syncthreads();
+    }
+  }
+};
+
+// ------------------------------------------------------------ phase epilogues
+//
+// Every epilogue walks the accumulators in groups of four consecutive rows of
+// one column: rows row0..row0+3 of column col. A mirrored (transposed) copy of
+// such a group is one contiguous 4-element store.
+
+template <class E>
+struct TileWalk {
+  // Calls f(row0, col, v[4]) for every 4-row group of the tile at (tile_r, tile_c).
+  template <class F>
+  static __device__ __forceinline__ void each(int64_t tile_r, int64_t tile_c,
+                                              f32x16 (&acc)[E::FM][E::FN], F&& f) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t wr = tile_r + E::wave_m(wave) * E::WM + 4 * (lane >> 5);
+    const int64_t wc = tile_c + E::wave_n(wave) * E::WN + (lane & 31);
+#pragma unroll
+    for (int i = 0; i < E::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < E::FN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                        acc[i][j][4 * g + 3]};
+          f(wr + i * 32 + 8 * g, wc + j * 32, v);
+        }
+  }
+};
+
+// Stores a symmetric m x m result tile: C[row][col] and the mirror C[col][row]
+// (off-diagonal tiles only). Entries outside the valid m x m block are 0.
+template <class T>
+__device__ __forceinline__ void store_sym(T* C, int64_t ld, int m, bool mirror, int64_t row0,
+                                          int64_t col, float v[4]) {
+  const bool cok = col < m;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (!(cok && row0 + q < m)) v[q] = 0.f;
+    Elem<T>::store(C + (row0 + q) * ld + col, v[q]);
+  }
+  if (mirror) Vec4<T>::store(C + col * ld + row0, v);
+}
+
+template <class E>
+__device__ void gram_tile(const PhaseArgs& args, const MatDev& d, int ti, int tj, void* smem) {
+  typedef typename E::T T;
+  const T* X = static_cast<const T*>(d.x[args.src]);
+  f32x16 acc[E::FM][E::FN];
+  E::run(X + (int64_t)ti * E::BM * d.np, d.np, X + (int64_t)tj * E::BN * d.np, d.np, d.np,
+         static_cast<T*>(smem), acc);
+  // First iteration: X holds the unscaled U, so A = s^2 U U^T.
+  float alpha = 1.f;
+  if (args.first) {
+    const float s = args.scale[&d - args.mats];
+    alpha = s * s;
+  }
+  T* A = static_cast<T*>(d.a);
+  const bool mirror = ti != tj;
+  TileWalk<E>::each((int64_t)ti * E::BM, (int64_t)tj * E::BN, acc,
+                    [&](int64_t row0, int64_t col, float v[4]) {
+                      for (int q = 0; q < 4; ++q) v[q] *= alpha;
+                      store_sym<T>(A, d.mp, d.m, mirror, row0, col, v);
+                    });
+}
+
+template <class E>
+__device__ void square_tile(const PhaseArgs& args, const MatDev& d, int ti, int tj, void* smem) {
+  typedef typename E::T T;
+  const T* A = static_cast<const T*>(d.a);
+  f32x16 acc[E::FM][E::FN];
+  E::run(A + (int64_t)ti * E::BM * d.mp, d.mp, A + (int64_t)tj * E::BN * d.mp, d.mp, d.mp,
+         static_cast<T*>(smem), acc);
+  T* B = static_cast<T*>(d.b);
+  const float cb = args.co.b, cc = args.co.c;
+  const bool mirror = ti != tj;
+  TileWalk<E>::each((int64_t)ti * E::BM, (int64_t)tj * E::BN, acc,
+                    [&](int64_t row0, int64_t col, float v[4]) {
+                      // B = b*A + c*(A*A), formed in fp32 and rounded once.
+                      for (int q = 0; q < 4; ++q)
+                        v[q] = cb * Elem<T>::load(A + (row0 + q) * d.mp + col) + cc * v[q];
+                      store_sym<T>(B, d.mp, d.m, mirror, row0, col, v);
+                    });
+}
+
+template <class E>
+__device__ void update_tile(const PhaseArgs& args, const MatDev& d, int ti, int tj, void* smem) {
+  typedef typename E::T T;
+  const int src = args.src, dst = src ^ 1;
+  const T* B = static_cast<const T*>(d.b);
+  const T* Xt = static_cast<const T*>(d.xt[src]);
+  f32x16 acc[E::FM][E::FN];
+  // (B X)[i][j] = sum_k B[i][k] X^T[j][k]
+  E::run(B + (int64_t)ti * E::BM * d.mp, d.mp, Xt + (int64_t)tj * E::BN * d.mp, d.mp, d.mp,
+         static_cast<T*>(smem), acc);
+  const T* X = static_cast<const T*>(d.x[src]);
+  const float ca = args.co.a;
+  // First iteration: X holds the unscaled U, and B was built from s*U, so
+  // X1 = s * (a U + B U).
+  const float xs = args.first ? args.scale[&d - args.mats] : 1.f;
+  const int m = d.m, n = d.n;
+  if (!args.last) {
+    T* Xo = static_cast<T*>(d.x[dst]);
+    T* Xto = static_cast<T*>(d.xt[dst]);
+    TileWalk<E>::each((int64_t)ti * E::BM, (int64_t)tj * E::BN, acc,
+                      [&](int64_t row0, int64_t col, float v[4]) {
+                        const bool cok = col < n;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                          const int64_t o = (row0 + q) * d.np + col;
+                          v[q] = (cok && row0 + q < m) ? xs * (ca * Elem<T>::load(X + o) + v[q]) : 0.f;
+                          Elem<T>::store(Xo + o, v[q]);
+                        }
+                        Vec4<T>::store(Xto + col * d.mp + row0, v);
+                      });
+    return;
+  }
+  // Last iteration: O = X_T (or X_T^T for a tall matrix).
+  // W -= lr*scale*O, delta = -lr*scale*O.
+  T* W = static_cast<T*>(d.w);
+  T* D = static_cast<T*>(d.delta);
+  const float ls = d.lr_scale;
+  const int64_t ldw = d.cols;
+  TileWalk<E>::each((int64_t)ti * E::BM, (int64_t)tj * E::BN, acc,
+                    [&](int64_t row0, int64_t col, float v[4]) {
+                      if (col >= n) return;
+#pragma unroll
+                      for (int q = 0; q < 4; ++q) {
+                        const int64_t r = row0 + q;
+                        if (r >= m) break;
+                        const float o = xs * (ca * Elem<T>::load(X + r * d.np + col) + v[q]);
+                        const int64_t wo = d.tall ? col * ldw + r : r * ldw + col;
+                        if (W) Elem<T>::store(W + wo, Elem<T>::load(W + wo) - ls * o);
+                        if (D) Elem<T>::store(D + wo, -ls * o);
+                      }
+                    });
+}
+
+// ------------------------------------------------------------ persistent phase kernel
+
+template <class E, int PH>
+__global__ void __launch_bounds__(E::NT) phase_kernel(PhaseArgs args) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[E::LDS_BYTES];
+  __shared__ int s_tile;
+  if (threadIdx.x == 0) s_tile = atomicAdd(args.counter, 1);
+  __syncthreads();
+  int t = s_tile;
+  while (t < args.n_tiles) {
+    const Tile tile = args.tiles[t];
+    const MatDev& d = args.mats[tile.mat];
+    const int ti = tile.ij >> 16, tj = tile.ij & 0xffff;
+    if (PH == kGram) gram_tile<E>(args, d, ti, tj, smem);
+    else if (PH == kSquare) square_tile<E>(args, d, ti, tj, smem);
+    else update_tile<E>(args, d, ti, tj, smem);
+    __syncthreads();  // every thread has read s_tile and finished with LDS
+    if (threadIdx.x == 0) s_tile = atomicAdd(args.counter, 1);
+    __syncthreads();
+    t = s_tile;
+  }
+}
+
+// ------------------------------------------------------------ elementwise kernels
+
+// Matrix of elementwise block b: the last i with prefix[i] <= b.
+__device__ __forceinline__ int find_mat(const int32_t* prefix, int n, int b) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (prefix[mid] <= b) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ float block_sum_256(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+// Fused momentum. One 64 x 64 tile of one matrix per workgroup of 256 threads.
+// Nothing here mixes elements of a tile, except the sum of squares.
+template <class T>
+__global__ void __launch_bounds__(256) momentum_kernel(EwArgs args) {
+  constexpr int TS = kEwTile;
+  __shared__ T tileU[TS][TS + (sizeof(T) == 2 ? 2 : 1)];
+  __shared__ float red[4];
+  const int tid = threadIdx.x;
+  if (blockIdx.x == 0)
+    for (int i = tid; i < args.n_counters; i += 256) args.counters[i] = 0;
+
+  const int mi = find_mat(args.prefix, args.n_mats, blockIdx.x);
+  const MatDev& d = args.mats[mi];
+  const int local = blockIdx.x - args.prefix[mi];
+  const int64_t r0 = (int64_t)(local / d.ew_tiles_c) * TS;
+  const int64_t c0 = (int64_t)(local % d.ew_tiles_c) * TS;
+  const int rows = d.rows, cols = d.cols;
+  const T* G = static_cast<const T*>(d.g);
+  T* Mo = static_cast<T*>(d.mom);
+  // U in its own orientation (rows x cols) and transposed (cols x rows).
+  T* Ub = static_cast<T*>(d.tall ? d.xt[0] : d.x[0]);
+  T* Utb = static_cast<T*>(d.tall ? d.x[0] : d.xt[0]);
+  const int64_t ldu = d.tall ? d.mp : d.np;
+  const int64_t ldut = d.tall ? d.np : d.mp;
+  const float beta = args.co.beta;
+  const bool nesterov = args.co.nesterov != 0;
+  const bool vec_ok = (cols & 3) == 0;
+
+  float ss = 0.f;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int lr = p * 16 + (tid >> 4), lc = (tid & 15) * 4;
+    const int64_t gr = r0 + lr, gc = c0 + lc;
+    float u[4] = {0.f, 0.f, 0.f, 0.f};
+    if (gr < rows) {
+      const int64_t o = gr * cols + gc;
+      if (vec_ok && gc + 3 < cols) {
+        float g[4], mm[4], mn[4];
+        Vec4<T>::load(G + o, g);
+        Vec4<T>::load(Mo + o, mm);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          mn[e] = beta * mm[e] + g[e];
+          u[e] = nesterov ? g[e] + beta * mn[e] : mn[e];
+        }
+        Vec4<T>::store(Mo + o, mn);
+        Vec4<T>::store(Ub + gr * ldu + gc, u);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (gc + e < cols) {
+            const float g = Elem<T>::load(G + o + e);
+            const float mn = beta * Elem<T>::load(Mo + o + e) + g;
+            u[e] = nesterov ? g + beta * mn : mn;
+            Elem<T>::store(Mo + o + e, mn);
+            Elem<T>::store(Ub + gr * ldu + gc + e, u[e]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      ss += u[e] * u[e];
+      T tv;
+      Elem<T>::store(&tv, u[e]);
+      tileU[lr][lc + e] = tv;
+    }
+  }
+  const float tot = block_sum_256(ss, red);  // contains a barrier: tileU is complete
+  if (tid == 0) args.partials[d.part_off + local] = tot;
+
+  // Transposed copy: row gc of U^T holds column gc of U.
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int lc = p * 16 + (tid >> 4), lr = (tid & 15) * 4;
+    const int64_t gc = c0 + lc, gr = r0 + lr;
+    if (gc >= cols) continue;
+    T* dst = Utb + gc * ldut + gr;
+    if (gr + 3 < rows) {
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = Elem<T>::load(&tileU[lr + e][lc]);
+      Vec4<T>::store(dst, v);
+    } else {
+      for (int e = 0; e < 4 && gr + e < rows; ++e) dst[e] = tileU[lr + e][lc];
+    }
+  }
+}
+
+// s = 1 / (||U||_F + eps) for one matrix per workgroup. The partials are summed
+// in fp64 in a fixed order, so the result does not depend on scheduling.
+__global__ void __launch_bounds__(256) norm_kernel(const MatDev* mats, const float* partials,
+                                                   float* scale, float eps) {
+  __shared__ double red[256];
+  const MatDev& d = mats[blockIdx.x];
+  double s = 0.0;
+  for (int i = threadIdx.x; i < d.n_parts; i += 256) s += (double)partials[d.part_off + i];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) scale[blockIdx.x] = (float)(1.0 / (sqrt(red[0]) + (double)eps));
+}
+
+// T = 0: O = s*U, so W -= lr*scale*s*U and delta = -lr*scale*s*U.
+template <class T>
+__global__ void __launch_bounds__(256) apply_kernel(EwArgs args) {
+  const int mi = find_mat(args.prefix, args.n_mats, blockIdx.x);
+  const MatDev& d = args.mats[mi];
+  const int local = blockIdx.x - args.prefix[mi];
+  const int64_t r0 = (int64_t)(local / d.ew_tiles_c) * kEwTile;
+  const int64_t c0 = (int64_t)(local % d.ew_tiles_c) * kEwTile;
+  const T* Ub = static_cast<const T*>(d.tall ? d.xt[0] : d.x[0]);
+  const int64_t ldu = d.tall ? d.mp : d.np;
+  T* W = static_cast<T*>(d.w);
+  T* D = static_cast<T*>(d.delta);
+  const float f = d.lr_scale * args.scale[mi];
+  for (int e = threadIdx.x; e < kEwTile * kEwTile; e += 256) {
+    const int64_t gr = r0 + e / kEwTile, gc = c0 + e % kEwTile;
+    if (gr >= d.rows || gc >= d.cols) continue;
+    const float o = f * Elem<T>::load(Ub + gr * ldu + gc);
+    const int64_t wo = gr * d.cols + gc;
+    if (W) Elem<T>::store(W + wo, Elem<T>::load(W + wo) - o);
+    if (D) Elem<T>::store(D + wo, -o);
+  }
+}
+
+// ------------------------------------------------------------ launchers
+
+hipError_t launch_momentum(int dtype, const EwArgs& args, int32_t n_blocks, hipStream_t s) {
+  if (dtype == 1) hipLaunchKernelGGL(momentum_kernel<u16>, dim3(n_blocks), dim3(256), 0, s, args);
+  else hipLaunchKernelGGL(momentum_kernel<float>, dim3(n_blocks), dim3(256), 0, s, args);
+  return hipGetLastError();
+}
+
+hipError_t launch_norm(const MatDev* mats, const float* partials, float* scale, int32_t n_mats,
+                       float eps, hipStream_t s) {
+  hipLaunchKernelGGL(norm_kernel, dim3(n_mats), dim3(256), 0, s, mats, partials, scale, eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_apply(int dtype, const EwArgs& args, int32_t n_blocks, hipStream_t s) {
+  if (dtype == 1) hipLaunchKernelGGL(apply_kernel<u16>, dim3(n_blocks), dim3(256), 0, s, args);
+  else hipLaunchKernelGGL(apply_kernel<float>, dim3(n_blocks), dim3(256), 0, s, args);
+  return hipGetLastError();
+}
+
+template <class E>
+static hipError_t launch_phase_e(Phase ph, const PhaseArgs& args, int32_t grid, hipStream_t s) {
+  switch (ph) {
+    case kGram: hipLaunchKernelGGL((phase_kernel<E, kGram>), dim3(grid), dim3(E::NT), 0, s, args); break;
+    case kSquare: hipLaunchKernelGGL((phase_kernel<E, kSquare>), dim3(grid), dim3(E::NT), 0, s, args); break;
+    default: hipLaunchKernelGGL((phase_kernel<E, kUpdate>), dim3(grid), dim3(E::NT), 0, s, args); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_phase(int dtype, Phase ph, const PhaseArgs& args, int32_t grid, hipStream_t s) {
+  return dtype == 1 ? launch_phase_e<EngineBF16>(ph, args, grid, s)
+                    : launch_phase_e<EngineF32>(ph, args, grid, s);
+}
+
+int gemm_blocks_per_cu(int dtype) {
+  // 147 KB of LDS per bf16 workgroup: one per CU. The fp32 engine uses
+  // 66 KB and 256 threads: two per CU.
+  return dtype == 1 ? 1 : 2;
+}
+
+}  // namespace muon

@@ -1,0 +1,207 @@
+"""ctypes binding of libmuon.so (include/muon.h), with the same names.
+
+It only marshals arguments: every step of the optimizer runs in the HIP
+library. PyTorch supplies device memory and the current stream. If the library
+is missing, the binding raises; there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Iterable, List, Optional, Sequence
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "_lib", "libmuon.so")
+
+MUON_OK = 0
+STATUS_NAMES = {0: "OK", -1: "INVALID_ARG", -2: "ALIAS", -3: "ALIGN", -4: "UNSUPPORTED",
+                -5: "HIP", -6: "OOM"}
+MUON_F32, MUON_BF16 = 0, 1
+KERNEL_KINDS = ("momentum", "norm", "gram", "square", "update", "apply")
+MUON_K_COUNT = len(KERNEL_KINDS)
+
+
+class muon_matrix(ctypes.Structure):
+    _fields_ = [("w", ctypes.c_void_p), ("g", ctypes.c_void_p), ("m", ctypes.c_void_p),
+                ("delta", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64)]
+
+
+class muon_hparams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("beta", ctypes.c_float), ("eps", ctypes.c_float),
+                ("a", ctypes.c_float), ("b", ctypes.c_float), ("c", ctypes.c_float),
+                ("ns_steps", ctypes.c_int32), ("nesterov", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+class MuonError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"muon: {STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+# Every function the header declares.
+EXPORTS = ("muon_hparams_default", "muon_plan", "muon_plan_workspace_bytes", "muon_step",
+           "muon_plan_destroy", "muon_last_error", "muon_plan_set_timing",
+           "muon_plan_kernel_times", "muon_plan_reset_timing", "muon_plan_info")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library. It raises if libmuon.so has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m matrix_optimizer_step_muon_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    c_int, c_i32, c_i64, c_vp = ctypes.c_int, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+    L.muon_hparams_default.argtypes = [ctypes.POINTER(muon_hparams)]
+    L.muon_plan.argtypes = [ctypes.POINTER(muon_matrix), c_i32, ctypes.POINTER(muon_hparams),
+                            ctypes.POINTER(c_vp)]
+    L.muon_plan_workspace_bytes.argtypes = [c_vp, ctypes.POINTER(ctypes.c_size_t)]
+    L.muon_step.argtypes = [c_vp, c_vp]
+    L.muon_plan_destroy.argtypes = [c_vp]
+    L.muon_last_error.argtypes = []
+    L.muon_last_error.restype = ctypes.c_char_p
+    L.muon_plan_set_timing.argtypes = [c_vp, c_i32]
+    L.muon_plan_kernel_times.argtypes = [c_vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(c_i64)]
+    L.muon_plan_reset_timing.argtypes = [c_vp]
+    L.muon_plan_info.argtypes = [c_vp, ctypes.POINTER(c_i64), ctypes.POINTER(c_i64)]
+    for name in EXPORTS:
+        if name != "muon_last_error":
+            getattr(L, name).restype = c_int
+    _lib = L
+    return L
+
+
+def last_error() -> str:
+    return lib().muon_last_error().decode()
+
+
+def check(status: int) -> None:
+    if status != MUON_OK:
+        raise MuonError(status, last_error())
+
+
+def hparams_default() -> muon_hparams:
+    hp = muon_hparams()
+    check(lib().muon_hparams_default(ctypes.byref(hp)))
+    return hp
+
+
+def make_hparams(lr=0.02, beta=0.95, eps=1e-7, coeffs=(3.4445, -4.7750, 2.0315),
+                 ns_steps=5, nesterov=True, dtype=MUON_BF16) -> muon_hparams:
+    a, b, c = coeffs
+    return muon_hparams(lr, beta, eps, a, b, c, int(ns_steps), int(bool(nesterov)), int(dtype))
+
+
+def plan_raw(descs: Sequence[muon_matrix], hp: muon_hparams) -> int:
+    """muon_plan over raw descriptors; returns the plan handle (an int)."""
+    arr = (muon_matrix * max(len(descs), 1))(*descs)
+    out = ctypes.c_void_p()
+    check(lib().muon_plan(arr, len(descs), ctypes.byref(hp), ctypes.byref(out)))
+    return out.value
+
+
+def step_raw(handle: int, stream: int = 0) -> None:
+    check(lib().muon_step(ctypes.c_void_p(handle), ctypes.c_void_p(stream)))
+
+
+def destroy_raw(handle: Optional[int]) -> None:
+    check(lib().muon_plan_destroy(ctypes.c_void_p(handle)))
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return MUON_BF16
+    if t.dtype == torch.float32:
+        return MUON_F32
+    raise MuonError(-4, f"unsupported tensor dtype {t.dtype}")
+
+
+class Plan:
+    """A static plan over a batch of ``(W, G, M[, delta])`` device tensors.
+
+    Tensors must be 2-D, contiguous, on one GPU, all bf16 or all fp32. They stay
+    referenced by the plan, since it keeps their addresses.
+    """
+
+    def __init__(self, mats: Iterable[Sequence], *, lr=0.02, beta=0.95, eps=1e-7,
+                 coeffs=(3.4445, -4.7750, 2.0315), ns_steps=5, nesterov=True):
+        self._handle = None
+        self._tensors: List = []
+        descs = []
+        dtype = None
+        for entry in mats:
+            W, G, M = entry[0], entry[1], entry[2]
+            D = entry[3] if len(entry) > 3 else None
+            ref = W if W is not None else D
+            code = _dtype_code(ref)
+            dtype = code if dtype is None else dtype
+            for t in (W, G, M, D):
+                if t is None:
+                    continue
+                if not t.is_cuda or not t.is_contiguous() or t.dim() != 2:
+                    raise MuonError(-1, "tensors must be contiguous 2-D device tensors")
+                if _dtype_code(t) != dtype or tuple(t.shape) != tuple(ref.shape):
+                    raise MuonError(-1, "tensors of a batch must share one dtype and shape per matrix")
+            self._tensors.append((W, G, M, D))
+            descs.append(muon_matrix(W.data_ptr() if W is not None else None, G.data_ptr(),
+                                     M.data_ptr(), D.data_ptr() if D is not None else None,
+                                     ref.shape[0], ref.shape[1]))
+        if not descs:
+            raise MuonError(-1, "empty batch")
+        self.hparams = make_hparams(lr, beta, eps, coeffs, ns_steps, nesterov, dtype)
+        self._handle = plan_raw(descs, self.hparams)
+
+    def step(self, stream=None) -> None:
+        import torch
+        if stream is None:
+            stream = torch.cuda.current_stream()
+        step_raw(self._handle, stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+    def workspace_bytes(self) -> int:
+        v = ctypes.c_size_t()
+        check(lib().muon_plan_workspace_bytes(ctypes.c_void_p(self._handle), ctypes.byref(v)))
+        return v.value
+
+    def info(self):
+        t = (ctypes.c_int64 * MUON_K_COUNT)()
+        g = (ctypes.c_int64 * MUON_K_COUNT)()
+        check(lib().muon_plan_info(ctypes.c_void_p(self._handle), t, g))
+        return {k: {"tiles": t[i], "grid": g[i]} for i, k in enumerate(KERNEL_KINDS)}
+
+    def set_timing(self, enable: bool) -> None:
+        check(lib().muon_plan_set_timing(ctypes.c_void_p(self._handle), int(bool(enable))))
+
+    def kernel_times(self):
+        """Per kernel kind: (total ms, launches), from HIP events on the step stream."""
+        ms = (ctypes.c_double * MUON_K_COUNT)()
+        n = (ctypes.c_int64 * MUON_K_COUNT)()
+        check(lib().muon_plan_kernel_times(ctypes.c_void_p(self._handle), ms, n))
+        return {k: (ms[i], n[i]) for i, k in enumerate(KERNEL_KINDS)}
+
+    def reset_timing(self) -> None:
+        check(lib().muon_plan_reset_timing(ctypes.c_void_p(self._handle)))
+
+    def close(self) -> None:
+        if self._handle is not None:
+            h, self._handle = self._handle, None
+            destroy_raw(h)
+        self._tensors = []
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()

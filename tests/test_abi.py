@@ -1,0 +1,172 @@
+"""The C ABI without a GPU: the library loads, it exports every function the
+header declares, and muon_plan rejects bad arguments before any HIP call."""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from matrix_optimizer_step_muon_amd import muon
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "muon.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(muon_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = header_functions()
+    for required in ("muon_plan", "muon_step", "muon_plan_destroy", "muon_last_error",
+                     "muon_plan_workspace_bytes", "muon_hparams_default"):
+        assert required in names
+    assert sorted(muon.EXPORTS) == names
+
+
+def test_library_exports_every_declared_symbol():
+    L = muon.lib()
+    for name in header_functions():
+        assert hasattr(L, name), name
+
+
+def test_hparams_default():
+    hp = muon.hparams_default()
+    assert hp.lr == pytest.approx(0.02) and hp.beta == pytest.approx(0.95)
+    assert hp.eps == pytest.approx(1e-7)
+    assert (hp.a, hp.b, hp.c) == pytest.approx((3.4445, -4.7750, 2.0315))
+    assert hp.ns_steps == 5 and hp.nesterov == 1 and hp.dtype == muon.MUON_BF16
+    assert muon.lib().muon_hparams_default(None) == -1
+
+
+def test_struct_layout_matches_header():
+    assert ctypes.sizeof(muon.muon_matrix) == 48
+    assert ctypes.sizeof(muon.muon_hparams) == 36
+
+
+# Fake, well-aligned device addresses. Validation rejects every case below
+# before any HIP call, so nothing is dereferenced.
+BASE = 0x7F0000000000
+
+
+def desc(i, rows=64, cols=128, elem=2, w=True, delta=False):
+    stride = 1 << 24
+    b = BASE + i * 4 * stride
+    return muon.muon_matrix(b if w else None, b + stride, b + 2 * stride,
+                            b + 3 * stride if delta else None, rows, cols)
+
+
+def plan_status(descs, hp=None, n=None):
+    hp = hp or muon.make_hparams()
+    arr = (muon.muon_matrix * max(len(descs), 1))(*descs)
+    out = ctypes.c_void_p(123)
+    st = muon.lib().muon_plan(arr, len(descs) if n is None else n, ctypes.byref(hp), ctypes.byref(out))
+    return st, out.value, muon.last_error()
+
+
+@pytest.mark.parametrize("case,status,msg", [
+    ("n0", -1, "n must be"),
+    ("rows0", -1, "rows and cols"),
+    ("cols_neg", -1, "rows and cols"),
+    ("g_null", -1, "g is NULL"),
+    ("m_null", -1, "m is NULL"),
+    ("w_delta_null", -1, "both NULL"),
+    ("lr_nan", -1, "lr is not finite"),
+    ("beta_one", -1, "beta must be"),
+    ("beta_neg", -1, "beta must be"),
+    ("eps_neg", -1, "eps must be"),
+    ("eps_inf", -1, "eps is not finite"),
+    ("steps_neg", -1, "ns_steps"),
+    ("nesterov_2", -1, "nesterov"),
+    ("dtype_7", -4, "dtype"),
+    ("misaligned", -3, "16-byte aligned"),
+    ("alias_within", -2, "overlaps"),
+    ("alias_across", -2, "overlaps"),
+    ("too_big", -1, "2^24"),
+])
+def test_plan_validation(case, status, msg):
+    d = [desc(0), desc(1)]
+    hp = muon.make_hparams()
+    n = None
+    if case == "n0":
+        n = 0
+    elif case == "rows0":
+        d[0].rows = 0
+    elif case == "cols_neg":
+        d[1].cols = -3
+    elif case == "g_null":
+        d[0].g = None
+    elif case == "m_null":
+        d[1].m = None
+    elif case == "w_delta_null":
+        d[0].w = None
+    elif case == "lr_nan":
+        hp.lr = math.nan
+    elif case == "beta_one":
+        hp.beta = 1.0
+    elif case == "beta_neg":
+        hp.beta = -0.1
+    elif case == "eps_neg":
+        hp.eps = -1e-7
+    elif case == "eps_inf":
+        hp.eps = math.inf
+    elif case == "steps_neg":
+        hp.ns_steps = -1
+    elif case == "nesterov_2":
+        hp.nesterov = 2
+    elif case == "dtype_7":
+        hp.dtype = 7
+    elif case == "misaligned":
+        d[1].m = d[1].m + 8
+    elif case == "alias_within":
+        d[0].m = d[0].g + 64
+    elif case == "alias_across":
+        d[1].w = d[0].w + 128
+    elif case == "too_big":
+        d[0].cols = (1 << 24) + 1
+    st, out, err = plan_status(d, hp, n)
+    assert st == status, err
+    assert msg in err
+    assert out is None          # *out is cleared on error
+
+
+def test_null_arguments():
+    L = muon.lib()
+    hp = muon.make_hparams()
+    out = ctypes.c_void_p()
+    assert L.muon_plan(None, 1, ctypes.byref(hp), ctypes.byref(out)) == -1
+    arr = (muon.muon_matrix * 1)(desc(0))
+    assert L.muon_plan(arr, 1, None, ctypes.byref(out)) == -1
+    assert L.muon_plan(arr, 1, ctypes.byref(hp), None) == -1
+    assert L.muon_step(None, None) == -1
+    assert L.muon_plan_destroy(None) == 0           # NULL-safe
+    assert L.muon_plan_workspace_bytes(None, None) == -1
+    assert L.muon_plan_set_timing(None, 1) == -1
+    assert L.muon_plan_kernel_times(None, None, None) == -1
+    assert L.muon_plan_info(None, None, None) == -1
+
+
+def test_adjacent_ranges_do_not_alias():
+    # Back-to-back ranges [p, p + bytes) and [p + bytes, ...) are legal.
+    rows, cols = 64, 128
+    nbytes = rows * cols * 2
+    b = BASE
+    d = muon.muon_matrix(b, b + nbytes, b + 2 * nbytes, b + 3 * nbytes, rows, cols)
+    st, out, err = plan_status([d])
+    # Validation passes, so the next failure (if any) comes from HIP.
+    assert st in (0, -5, -6), err
+    if st == 0:
+        muon.destroy_raw(out)
+
+
+def test_no_gpu_valid_plan_reports_hip_error_not_crash():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    st, out, err = plan_status([desc(0)])
+    assert st == -5 and out is None
+    assert err.startswith("hip")

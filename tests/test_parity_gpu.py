@@ -1,0 +1,148 @@
+"""GPU parity of the HIP path against the fp64 oracle, through the C ABI.
+
+Bars: relative Frobenius error <= 1e-4 for the fp32 path and <= 2e-2 for the
+bf16 path, checked on:
+- O, recovered from the delta output;
+- the momentum buffer M';
+- the weights W'.
+Sizes span several tiles and ragged tails. The last test runs the full
+Qwen3-32B layer in the same plan and launch configuration that bench.py times,
+and checks sampled matrices and properties that hold at any size.
+"""
+
+import numpy as np
+import pytest
+
+from gpu_helpers import TOL, compare, gpu_step, log, oracle_step
+from matrix_optimizer_step_muon_amd import workloads as wl
+from oracle import muon_ref as ref
+
+pytestmark = pytest.mark.gpu
+
+
+def run_case(wload, label, steps=1, **kw):
+    inputs = wl.generate(wload)
+    hp = wload.hparams()
+    log(f"case {label}: {len(inputs)} matrices, dtype {wload.dtype}, hp {hp}")
+    gpu = gpu_step(inputs, wload.dtype, hp, steps=steps, **kw)
+    want = oracle_step(inputs, wload.dtype, hp, steps=steps)
+    return compare(gpu, want, wload.dtype, hp, inputs, label)
+
+
+def test_tiny_f32_batch():
+    run_case(wl.WORKLOADS["tiny_f32_16x128x256"], "tiny_f32_16x128x256")
+
+
+def test_qwen3_1p7b_layer_bf16():
+    run_case(wl.WORKLOADS["qwen3_1p7b_layer"], "qwen3_1p7b_layer")
+
+
+RAGGED = [(1000, 3000), (3000, 1000), (1, 5), (5, 1), (1, 1), (256, 256), (300, 700),
+          (700, 300), (513, 512), (129, 1030), (64, 2048)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_ragged_heterogeneous_batch(dtype):
+    w = wl.custom_workload(f"ragged_{dtype}", RAGGED, dtype, seed=21,
+                           g_std=1.0 if dtype == "f32" else 1e-3, w_std=0.02)
+    run_case(w, f"ragged_{dtype}")
+
+
+@pytest.mark.parametrize("ns_steps", [0, 1, 2])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_ns_step_counts(dtype, ns_steps):
+    w = wl.custom_workload(f"steps{ns_steps}_{dtype}", [(384, 640), (640, 384), (200, 200)], dtype,
+                           seed=31, ns_steps=ns_steps)
+    run_case(w, f"ns_steps={ns_steps} {dtype}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_without_nesterov(dtype):
+    w = wl.custom_workload(f"plain_{dtype}", [(512, 768), (768, 512)], dtype, seed=41, nesterov=False)
+    run_case(w, f"nesterov=False {dtype}")
+
+
+def test_zero_gradient_and_momentum_give_zero_update():
+    shapes = [(300, 500), (500, 300)]
+    inputs = [(wl.to_storage(wl.draw(5, i, 1, s, 0.02), "bf16"),
+               wl.to_storage(np.zeros(s, np.float32), "bf16"),
+               wl.to_storage(np.zeros(s, np.float32), "bf16")) for i, s in enumerate(shapes)]
+    gpu = gpu_step(inputs, "bf16", dict(lr=0.02, beta=0.95))
+    for (Wg, Mg, Dg), (W, _, _) in zip(gpu, inputs):
+        np.testing.assert_array_equal(Wg, W)
+        assert not np.any(wl.stored_to_f64(Dg, "bf16")), "delta must be exactly zero"
+        assert not np.any(wl.stored_to_f64(Mg, "bf16"))
+
+
+def test_two_consecutive_steps_carry_momentum():
+    w = wl.custom_workload("two_steps", [(512, 1024), (1024, 512)], "bf16", seed=51)
+    inputs = wl.generate(w)
+    g2 = [wl.to_storage(wl.draw(99, i, 0, s, 1e-3), "bf16") for i, s in enumerate(w.shapes)]
+    grads = [None, g2]
+    hp = w.hparams()
+    gpu = gpu_step(inputs, "bf16", hp, steps=2, grads=grads)
+    want = oracle_step(inputs, "bf16", hp, steps=2, grads=grads)
+    compare(gpu, want, "bf16", hp, inputs, "two steps")
+
+
+def test_result_is_independent_of_descriptor_order_and_deterministic():
+    w = wl.custom_workload("order", [(256, 768), (768, 256), (512, 512), (100, 900)], "bf16", seed=61)
+    inputs = wl.generate(w)
+    hp = w.hparams()
+    a = gpu_step(inputs, "bf16", hp)
+    b = gpu_step(inputs, "bf16", hp, order=[3, 1, 0, 2])
+    c = gpu_step(inputs, "bf16", hp)
+    for x, y, z in zip(a, b, c):
+        for u, v, t in zip(x, y, z):
+            np.testing.assert_array_equal(u, v)
+            np.testing.assert_array_equal(u, t)
+
+
+def test_delta_only_mode_leaves_no_weight_write():
+    w = wl.custom_workload("delta_only", [(640, 384)], "bf16", seed=71)
+    inputs = wl.generate(w)
+    hp = w.hparams()
+    gpu = gpu_step(inputs, "bf16", hp, with_w=False)
+    want = oracle_step(inputs, "bf16", hp)
+    compare(gpu, want, "bf16", hp, inputs, "delta only")
+
+
+def test_qwen3_32b_layer_full_size_sampled():
+    """The full Qwen3-32B layer in one plan, as bench.py times it.
+
+    Checked here:
+    - k and v (1024 x 5120) against the oracle in full;
+    - M' of every matrix on 20000 sampled elements against the elementwise
+      definition;
+    - W' + delta consistency everywhere;
+    - for every matrix, the Gram matrix of O has eigenvalues in the square of
+      the quintic's reachable interval (well-conditioned Gaussian inputs).
+    """
+    import torch
+    wload = wl.WORKLOADS["qwen3_32b_layer"]
+    hp = wload.hparams()
+    log("case qwen3_32b_layer: generating inputs")
+    inputs = wl.generate(wload)
+    log("case qwen3_32b_layer: running the HIP step")
+    gpu = gpu_step(inputs, "bf16", hp)
+    sample = [1, 2]
+    log("case qwen3_32b_layer: oracle on k and v")
+    want = oracle_step([inputs[i] for i in sample], "bf16", hp)
+    compare([gpu[i] for i in sample], want, "bf16", hp, [inputs[i] for i in sample], "qwen3_32b k,v")
+    rng = np.random.default_rng(0)
+    lo, top = 0.681831, 1.202369
+    for i, ((W, G, M), (Wg, Mg, Dg)) in enumerate(zip(inputs, gpu)):
+        r, c = W.shape
+        idx = rng.integers(0, r * c, 20000)
+        m_ref = 0.95 * wl.stored_to_f64(M.reshape(-1)[idx], "bf16") + wl.stored_to_f64(G.reshape(-1)[idx], "bf16")
+        assert wl.rel_fro(wl.stored_to_f64(Mg.reshape(-1)[idx], "bf16"), m_ref) < 4e-3
+        # W' and delta are each rounded once to bf16 from the same fp32 update,
+        # so W' - (W + delta) is within half an ulp of W' plus half an ulp of delta.
+        Wf, Wgf, Df = (wl.stored_to_f64(x, "bf16") for x in (W, Wg, Dg))
+        assert np.all(np.abs(Wgf - (Wf + Df)) <= (np.abs(Wgf) + np.abs(Df)) * 2.0 ** -8 + 1e-30)
+        O = torch.from_numpy(-Df / (hp["lr"] * ref.update_scale(r, c))).cuda().float()
+        O = O if r <= c else O.T
+        ev = torch.linalg.eigvalsh((O @ O.T).double()).cpu().numpy()
+        sv = np.sqrt(np.clip(ev, 0, None))
+        log(f"qwen3_32b matrix {i} {r}x{c}: singular values of O in [{sv.min():.4f}, {sv.max():.4f}]")
+        assert sv.min() > lo * 0.97 and sv.max() < top * 1.03
