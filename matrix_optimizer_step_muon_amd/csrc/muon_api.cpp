@@ -15,6 +15,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 #include <utility>
@@ -50,6 +51,7 @@ struct muon_plan_s {
   int n = 0;
   int device = 0;
   int tile = muon::kTileBF16;
+  int variant = muon::kGemmBK64;
 
   std::vector<muon::MatDev> mats;  // host copy (device pointers inside)
   void* ws = nullptr;
@@ -62,6 +64,7 @@ struct muon_plan_s {
   int32_t* d_counters = nullptr;
   int32_t n_counters = 0;
   muon::Tile* d_tiles[3] = {nullptr, nullptr, nullptr};
+  int32_t* d_qoff = nullptr;  // 3 x (kQueues + 1) queue offsets
   int32_t n_tiles[3] = {0, 0, 0};
   int32_t grid[3] = {0, 0, 0};
   int32_t ew_blocks = 0;
@@ -213,31 +216,57 @@ muon_status muon_plan(const muon_matrix* mats, int32_t n, const muon_hparams* hp
   const size_t o_prefix = take(sizeof(int32_t) * (n + 1));
   const size_t o_parts = take(sizeof(float) * std::max(parts, 1));
   const size_t o_scale = take(sizeof(float) * n);
-  p->n_counters = std::max(3 * hp->ns_steps, 1);
+  p->n_counters = std::max(3 * hp->ns_steps * muon::kQueues, 1);
   const size_t o_ctr = take(sizeof(int32_t) * p->n_counters);
 
-  // Tile tables, each sorted longest first. Every tile of a phase has the
-  // same area, so the cost is the contraction length K. Ties keep
-  // (matrix, tile row, tile col) order.
-  struct HT { int64_t cost; int32_t mat, ti, tj; };
-  std::vector<HT> tl[3];
+  // Tile tables. Each phase's tiles are cut into blocks of kBlockRows x
+  // kBlockCols tiles of one matrix. Blocks are dealt longest first to the
+  // least-loaded of the kQueues per-XCD queues: the LPT rule, with a block's
+  // cost = its multiply-adds = tiles x tile area x K. All tiles of a phase have
+  // the same area, so the cost is tiles x K. Ties keep (matrix, block) order,
+  // and a block's tiles stay in row-major order.
+  struct Block { int64_t cost; std::vector<muon::Tile> tiles; };
+  std::vector<Block> blocks[3];
   for (int32_t i = 0; i < n; ++i) {
     const muon::MatDev& d = p->mats[i];
-    const int32_t tm = d.mp / T, tn = d.np / T;
-    for (int32_t a = 0; a < tm; ++a)
-      for (int32_t b = a; b < tm; ++b) {
-        tl[muon::kGram].push_back({d.np, i, a, b});
-        tl[muon::kSquare].push_back({d.mp, i, a, b});
-      }
-    for (int32_t a = 0; a < tm; ++a)
-      for (int32_t b = 0; b < tn; ++b) tl[muon::kUpdate].push_back({d.mp, i, a, b});
+    const int32_t tm = int32_t(d.mp / T), tn = int32_t(d.np / T);
+    for (int ph = 0; ph < 3; ++ph) {
+      const int32_t cols = ph == muon::kUpdate ? tn : tm;
+      const int64_t K = ph == muon::kGram ? d.np : d.mp;
+      for (int32_t r0 = 0; r0 < tm; r0 += muon::kBlockRows)
+        for (int32_t c0 = 0; c0 < cols; c0 += muon::kBlockCols) {
+          Block b{0, {}};
+          for (int32_t a = r0; a < std::min(tm, r0 + muon::kBlockRows); ++a)
+            for (int32_t c = c0; c < std::min(cols, c0 + muon::kBlockCols); ++c)
+              if (ph == muon::kUpdate || c >= a) b.tiles.push_back({i, (a << 16) | c});
+          if (b.tiles.empty()) continue;
+          b.cost = int64_t(b.tiles.size()) * K;
+          blocks[ph].push_back(std::move(b));
+        }
+    }
   }
   size_t o_tiles[3];
+  const size_t o_qoff = take(sizeof(int32_t) * 3 * (muon::kQueues + 1));
   std::vector<muon::Tile> tiles[3];
+  std::vector<int32_t> qoff(3 * (muon::kQueues + 1), 0);
   for (int ph = 0; ph < 3; ++ph) {
-    std::stable_sort(tl[ph].begin(), tl[ph].end(), [](const HT& x, const HT& y) { return x.cost > y.cost; });
-    tiles[ph].reserve(tl[ph].size());
-    for (const HT& h : tl[ph]) tiles[ph].push_back({h.mat, (h.ti << 16) | h.tj});
+    std::stable_sort(blocks[ph].begin(), blocks[ph].end(),
+                     [](const Block& x, const Block& y) { return x.cost > y.cost; });
+    std::vector<std::vector<muon::Tile>> q(muon::kQueues);
+    int64_t load[muon::kQueues] = {};
+    for (const Block& b : blocks[ph]) {
+      int best = 0;
+      for (int k = 1; k < muon::kQueues; ++k)
+        if (load[k] < load[best]) best = k;
+      load[best] += b.cost;
+      q[best].insert(q[best].end(), b.tiles.begin(), b.tiles.end());
+    }
+    int32_t* qo = &qoff[ph * (muon::kQueues + 1)];
+    for (int k = 0; k < muon::kQueues; ++k) {
+      qo[k] = int32_t(tiles[ph].size());
+      tiles[ph].insert(tiles[ph].end(), q[k].begin(), q[k].end());
+    }
+    qo[muon::kQueues] = int32_t(tiles[ph].size());
     p->n_tiles[ph] = int32_t(tiles[ph].size());
     o_tiles[ph] = take(sizeof(muon::Tile) * std::max<size_t>(tiles[ph].size(), 1));
   }
@@ -249,7 +278,9 @@ muon_status muon_plan(const muon_matrix* mats, int32_t n, const muon_hparams* hp
   int n_cu = 0;
   e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, p->device);
   if (e != hipSuccess) { free_plan(p); return hip_fail(e, "hipDeviceGetAttribute"); }
-  const int32_t resident = n_cu * muon::gemm_blocks_per_cu(p->dtype);
+  // MUON_GEMM_VARIANT=0|1 picks the bf16 engine pipeline (a tuning knob).
+  if (const char* v = std::getenv("MUON_GEMM_VARIANT")) p->variant = std::atoi(v) == 1 ? muon::kGemmBK32 : muon::kGemmBK64;
+  const int32_t resident = n_cu * muon::gemm_blocks_per_cu(p->dtype, p->variant);
   for (int ph = 0; ph < 3; ++ph) p->grid[ph] = std::max(1, std::min(p->n_tiles[ph], resident));
 
   e = hipMalloc(&p->ws, p->ws_bytes);
@@ -277,10 +308,12 @@ muon_status muon_plan(const muon_matrix* mats, int32_t n, const muon_hparams* hp
   p->d_scale = reinterpret_cast<float*>(base + o_scale);
   p->d_counters = reinterpret_cast<int32_t*>(base + o_ctr);
   for (int ph = 0; ph < 3; ++ph) p->d_tiles[ph] = reinterpret_cast<muon::Tile*>(base + o_tiles[ph]);
+  p->d_qoff = reinterpret_cast<int32_t*>(base + o_qoff);
 
   struct Up { void* dst; const void* src; size_t bytes; };
-  const Up ups[5] = {
+  const Up ups[6] = {
       {p->d_mats, p->mats.data(), sizeof(muon::MatDev) * n},
+      {p->d_qoff, qoff.data(), sizeof(int32_t) * qoff.size()},
       {p->d_prefix, prefix.data(), sizeof(int32_t) * (n + 1)},
       {p->d_tiles[0], tiles[0].data(), sizeof(muon::Tile) * tiles[0].size()},
       {p->d_tiles[1], tiles[1].data(), sizeof(muon::Tile) * tiles[1].size()},
@@ -394,10 +427,11 @@ muon_status muon_step(muon_plan_t p, void* stream) {
   }
   for (int it = 0; it < T; ++it) {
     for (int ph = 0; ph < 3; ++ph) {
-      muon::PhaseArgs a{p->d_mats, p->d_tiles[ph], p->n_tiles[ph], p->d_counters + 3 * it + ph, p->d_scale,
-                        it & 1, it == 0, it == T - 1, co};
+      muon::PhaseArgs a{p->d_mats, p->d_tiles[ph], p->d_qoff + ph * (muon::kQueues + 1),
+                        p->d_counters + (3 * it + ph) * muon::kQueues, p->d_scale, it & 1, it == 0,
+                        it == T - 1, co};
       run(MUON_K_GRAM + ph,
-          [&] { return muon::launch_phase(p->dtype, muon::Phase(ph), a, p->grid[ph], s); });
+          [&] { return muon::launch_phase(p->dtype, p->variant, muon::Phase(ph), a, p->grid[ph], s); });
     }
   }
   if (cur != p->device) (void)hipSetDevice(cur);

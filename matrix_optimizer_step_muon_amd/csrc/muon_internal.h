@@ -14,6 +14,15 @@ constexpr int kTileBF16 = 256;  // bf16 engine: 256 x 256 output tiles, K step 6
 constexpr int kTileF32 = 128;   // fp32 engine: 128 x 128 output tiles, K step 32
 constexpr int kEwTile = 64;     // elementwise kernels: 64 x 64 tiles
 
+// GEMM work queues: one per XCD. Persistent workgroup w serves queue
+// w % kQueues first (workgroups are dispatched to the 8 XCDs round-robin), then
+// steals from the others. Each queue holds whole blocks of kBlockRows x
+// kBlockCols tiles, so concurrently running tiles on one XCD share operand
+// panels in that XCD's L2.
+constexpr int kQueues = 8;
+constexpr int kBlockRows = 4;
+constexpr int kBlockCols = 8;
+
 // One matrix of the batch as the kernels see it. X is the m x n orientation
 // of U (m = min(rows, cols)): U itself, or U^T when rows > cols.
 struct MatDev {
@@ -54,9 +63,9 @@ enum Phase { kGram = 0, kSquare = 1, kUpdate = 2 };
 // Arguments of one persistent GEMM-phase launch.
 struct PhaseArgs {
   const MatDev* mats;
-  const Tile* tiles;   // LPT-ordered tile list of this phase
-  int32_t n_tiles;
-  int32_t* counter;    // work-queue head of this launch (zeroed by the momentum kernel)
+  const Tile* tiles;     // the kQueues per-XCD tile lists of this phase, concatenated
+  const int32_t* qoff;   // kQueues + 1 offsets of those lists in `tiles`
+  int32_t* counter;      // kQueues queue heads of this launch (zeroed by the momentum kernel)
   const float* scale;  // per-matrix 1/(||U||_F + eps)
   int32_t src;         // ping/pong index read this iteration
   int32_t first;       // first iteration: fold the norm scale in
@@ -80,9 +89,14 @@ hipError_t launch_momentum(int dtype, const EwArgs& args, int32_t n_blocks, hipS
 hipError_t launch_norm(const MatDev* mats, const float* partials, float* scale, int32_t n_mats,
                        float eps, hipStream_t s);
 hipError_t launch_apply(int dtype, const EwArgs& args, int32_t n_blocks, hipStream_t s);
-hipError_t launch_phase(int dtype, Phase ph, const PhaseArgs& args, int32_t grid, hipStream_t s);
+// bf16 GEMM engine pipelines (8 waves of 128 x 64 each): K step 32 with a
+// ring of 4 LDS stages, or K step 64 with 2 stages.
+enum GemmVariant { kGemmBK64 = 0, kGemmBK32 = 1 };
+
+hipError_t launch_phase(int dtype, int variant, Phase ph, const PhaseArgs& args, int32_t grid,
+                        hipStream_t s);
 
 // Workgroups per CU that the persistent GEMM kernels can keep resident.
-int gemm_blocks_per_cu(int dtype);
+int gemm_blocks_per_cu(int dtype, int variant);
 
 }  // namespace muon

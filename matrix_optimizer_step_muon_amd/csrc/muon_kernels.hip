@@ -39,11 +39,28 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // ------------------------------------------------------------ element access
+//
+// Every global access goes through an address_space(1) pointer, so it
+// compiles to global_load / global_store. Generic (flat) accesses would also
+// count against the LDS wait counter and serialise the GEMM pipeline.
 
-__device__ __forceinline__ float bf16_to_f32(u16 v) { return __uint_as_float((uint32_t)v << 16); }
+#define MUON_INLINE __device__ __forceinline__ __attribute__((always_inline))
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef u32x4 __attribute__((address_space(1))) g_u32x4;
+typedef u32x2 __attribute__((address_space(1))) g_u32x2;
+typedef f32x4 __attribute__((address_space(1))) g_f32x4;
+typedef u16 __attribute__((address_space(1))) g_u16;
+typedef float __attribute__((address_space(1))) g_f32;
+
+MUON_INLINE u32x4 gload16(const void* p) { return *((const g_u32x4*)(p)); }
+
+MUON_INLINE float bf16_to_f32(u16 v) { return __uint_as_float((uint32_t)v << 16); }
 
 // Round to nearest even; NaN stays a (quiet) NaN.
-__device__ __forceinline__ u16 f32_to_bf16(float f) {
+MUON_INLINE u16 f32_to_bf16(float f) {
   uint32_t u = __float_as_uint(f);
   if ((u & 0x7fffffffu) > 0x7f800000u) return (u16)((u >> 16) | 0x40u);
   u += 0x7fffu + ((u >> 16) & 1u);
@@ -52,38 +69,43 @@ __device__ __forceinline__ u16 f32_to_bf16(float f) {
 
 template <class T> struct Elem;
 template <> struct Elem<float> {
-  static __device__ __forceinline__ float load(const float* p) { return *p; }
-  static __device__ __forceinline__ void store(float* p, float v) { *p = v; }
-  static __device__ __forceinline__ float round(float v) { return v; }
+  static MUON_INLINE float load(const float* p) { return *((const g_f32*)(p)); }
+  static MUON_INLINE void store(float* p, float v) { *((g_f32*)(p)) = v; }
+  static MUON_INLINE float lds_load(const float* p) { return *p; }
+  static MUON_INLINE float round(float v) { return v; }
+  static MUON_INLINE float to_storage(float v) { return v; }
 };
 template <> struct Elem<u16> {
-  static __device__ __forceinline__ float load(const u16* p) { return bf16_to_f32(*p); }
-  static __device__ __forceinline__ void store(u16* p, float v) { *p = f32_to_bf16(v); }
-  static __device__ __forceinline__ float round(float v) { return bf16_to_f32(f32_to_bf16(v)); }
+  static MUON_INLINE float load(const u16* p) { return bf16_to_f32(*((const g_u16*)(p))); }
+  static MUON_INLINE void store(u16* p, float v) { *((g_u16*)(p)) = f32_to_bf16(v); }
+  static MUON_INLINE float lds_load(const u16* p) { return bf16_to_f32(*p); }
+  static MUON_INLINE float round(float v) { return bf16_to_f32(f32_to_bf16(v)); }
+  static MUON_INLINE u16 to_storage(float v) { return f32_to_bf16(v); }
 };
 
 // Four consecutive elements, as one 8-byte (bf16) or 16-byte (fp32) access.
 template <class T> struct Vec4;
 template <> struct Vec4<float> {
-  static __device__ __forceinline__ void load(const float* p, float v[4]) {
-    float4 t = *reinterpret_cast<const float4*>(p);
-    v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+  static MUON_INLINE void load(const float* p, float v[4]) {
+    f32x4 t = *((const g_f32x4*)(p));
+    v[0] = t[0]; v[1] = t[1]; v[2] = t[2]; v[3] = t[3];
   }
-  static __device__ __forceinline__ void store(float* p, const float v[4]) {
-    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  static MUON_INLINE void store(float* p, const float v[4]) {
+    f32x4 t = {v[0], v[1], v[2], v[3]};
+    *((g_f32x4*)(p)) = t;
   }
 };
 template <> struct Vec4<u16> {
-  static __device__ __forceinline__ void load(const u16* p, float v[4]) {
-    uint2 t = *reinterpret_cast<const uint2*>(p);
-    v[0] = __uint_as_float(t.x << 16); v[1] = __uint_as_float(t.x & 0xffff0000u);
-    v[2] = __uint_as_float(t.y << 16); v[3] = __uint_as_float(t.y & 0xffff0000u);
+  static MUON_INLINE void load(const u16* p, float v[4]) {
+    u32x2 t = *((const g_u32x2*)(p));
+    v[0] = __uint_as_float(t[0] << 16); v[1] = __uint_as_float(t[0] & 0xffff0000u);
+    v[2] = __uint_as_float(t[1] << 16); v[3] = __uint_as_float(t[1] & 0xffff0000u);
   }
-  static __device__ __forceinline__ void store(u16* p, const float v[4]) {
-    uint2 t;
-    t.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-    t.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-    *reinterpret_cast<uint2*>(p) = t;
+  static MUON_INLINE void store(u16* p, const float v[4]) {
+    u32x2 t;
+    t[0] = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+    t[1] = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+    *((g_u32x2*)(p)) = t;
   }
 };
 
@@ -93,21 +115,66 @@ template <> struct Vec4<u16> {
 // (P, Q row-major, K a multiple of BK), and leaves it in MFMA accumulators.
 // Accumulator layout of a 32 x 32 MFMA block, element r of lane l:
 //   column = l % 32,  row = 8*(r/4) + 4*(l/32) + r%4.
+// The engines differ in their wave layout. WAVES_M x WAVES_N waves each own a
+// WM x WN sub-tile; fewer, larger wave tiles read less LDS per flop.
 
+// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4).
+// Lane l's bytes land at LDS address lds + 16*l, so one wave instruction
+// fills 1 KB of LDS. It is issued from inline asm, with M0 saved and restored
+// around it. The compiler then does not track these loads, and would not put a
+// conservative vmcnt(0) in front of every LDS read. The engine waits for them
+// itself, with the exact counts of its ring of stages. Untracked loads can
+// only make the compiler's own vmcnt waits stricter, never looser.
+MUON_INLINE void dma16(const void* g, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(g), "s"(lds)
+      : "memory");
+}
+
+template <int N>
+MUON_INLINE void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// LDS rows hold BK bf16: S = BK/8 16-byte slots. The slot of chunk c of row
+// r is c ^ swz(r). With these swizzles, the rows read by any 8 (32-bank model)
+// or 16 (64-bank model) consecutive lanes of an MFMA fragment read hit
+// distinct banks. Both depend only on r % 32, so every 32-row fragment block
+// shares one set of offsets.
+template <int S>
+MUON_INLINE int lds_swizzle(int r) {
+  if (S == 4) return ((r >> 1) ^ (r >> 3)) & 3;
+  return (r & 7) ^ ((r >> 3) & 1);
+}
+
+template <int WAVES_M, int WAVES_N, int BK_, int STAGES_>
 struct EngineBF16 {
   typedef u16 T;
-  static constexpr int BM = 256, BN = 256, BK = 64, NT = 512;
-  static constexpr int WM = 128, WN = 64;    // wave tile: 8 waves as 2 x 4
+  static constexpr int BM = 256, BN = 256, BK = BK_;
+  static constexpr int STAGES = STAGES_;  // loads run STAGES - 1 K steps ahead
+  static constexpr int NT = 64 * WAVES_M * WAVES_N;
+  static constexpr int NW = NT / 64;
+  static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   static constexpr int FM = WM / 32, FN = WN / 32;
-  static constexpr int LDS_STRIDE = BK + 8;  // u16; 144-byte rows avoid bank conflicts
-  static constexpr int STAGE = (BM + BN) * LDS_STRIDE;
-  static constexpr int LDS_BYTES = 2 * STAGE * 2;
-  static __device__ __forceinline__ int wave_m(int w) { return w >> 2; }
-  static __device__ __forceinline__ int wave_n(int w) { return w & 3; }
+  static constexpr int S = BK / 8;                  // 16-byte slots per LDS row
+  static constexpr int ROW = BK * 2;                // LDS row bytes
+  static constexpr int RPI = 1024 / ROW;            // rows per DMA wave instruction
+  static constexpr int OP_BYTES = BM * ROW;         // one operand tile of one stage
+  static constexpr int STAGE_BYTES = 2 * OP_BYTES;  // P and Q
+  static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+  static constexpr int DPW = OP_BYTES / 1024 / NW;  // DMA instructions per wave per operand
+  static constexpr bool kStageTile = true;          // epilogue operand tiles go through LDS
+  static MUON_INLINE int wave_m(int w) { return w / WAVES_N; }
+  static MUON_INLINE int wave_n(int w) { return w % WAVES_N; }
 
-  static __device__ __forceinline__ void run(const u16* __restrict__ P, int64_t ldp,
-                                             const u16* __restrict__ Q, int64_t ldq, int K,
-                                             u16* smem, f32x16 (&acc)[FM][FN]) {
+  static MUON_INLINE void run(const u16* __restrict__ P, int64_t ldp, const u16* __restrict__ Q,
+                              int64_t ldq, int K, u16* smem, f32x16 (&acc)[FM][FN]) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave_m(wave), wn = wave_n(wave);
 #pragma unroll
@@ -117,58 +184,69 @@ struct EngineBF16 {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    // Global -> register staging: each operand tile is BM rows x 128 bytes;
-    // a thread moves 4 16-byte chunks of each, 8 threads per row (coalesced).
-    uint4 rp[4], rq[4];
-    auto gload = [&](int k0) {
+    // DMA plan: instruction (wave, p) of an operand fills rows
+    // RPI*(wave*DPW + p) .. +RPI of the stage. Lane l carries row + l/S, slot
+    // l%S, i.e. the global chunk slot ^ swz(row).
+    const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
+    const u16* gp[DPW];
+    const u16* gq[DPW];
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const int q = tid + p * NT, row = q >> 3, ch = q & 7;
-        rp[p] = *reinterpret_cast<const uint4*>(P + row * ldp + k0 + ch * 8);
-        rq[p] = *reinterpret_cast<const uint4*>(Q + row * ldq + k0 + ch * 8);
-      }
-    };
-    auto sstore = [&](int s) {
-      u16* sp = smem + s * STAGE;
-      u16* sq = sp + BM * LDS_STRIDE;
+    for (int p = 0; p < DPW; ++p) {
+      const int row = (wave * DPW + p) * RPI + lane / S;
+      const int ch = (lane % S) ^ lds_swizzle<S>(row);
+      gp[p] = P + row * ldp + ch * 8;
+      gq[p] = Q + row * ldq + ch * 8;
+    }
+    auto issue = [&](int kt) __attribute__((always_inline)) {
+      const uint32_t st = lds_base + (kt % STAGES) * STAGE_BYTES;
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const int q = tid + p * NT, row = q >> 3, ch = q & 7;
-        *reinterpret_cast<uint4*>(sp + row * LDS_STRIDE + ch * 8) = rp[p];
-        *reinterpret_cast<uint4*>(sq + row * LDS_STRIDE + ch * 8) = rq[p];
+      for (int p = 0; p < DPW; ++p) {
+        const uint32_t off = (wave * DPW + p) * 1024;
+        dma16(gp[p] + kt * BK, __builtin_amdgcn_readfirstlane(st + off));
+        dma16(gq[p] + kt * BK, __builtin_amdgcn_readfirstlane(st + OP_BYTES + off));
       }
     };
 
+    // Fragment reads: lane l reads row l % 32 of each 32-row block, 16-byte
+    // chunk 2*kk + l/32, at slot chunk ^ swz(row).
+    const int r32 = lane & 31, h = lane >> 5, sw = lds_swizzle<S>(r32);
+    const unsigned char* sb = reinterpret_cast<const unsigned char*>(smem);
+
     const int KT = K / BK;
-    gload(0);
-    sstore(0);
-    __syncthreads();
+    constexpr int AHEAD = STAGES - 1;
+    constexpr int PS = 2 * DPW;  // DMA instructions per wave per stage
+#pragma unroll
+    for (int k = 0; k < AHEAD; ++k)
+      if (k < KT) issue(k);
     for (int kt = 0; kt < KT; ++kt) {
-      const int s = kt & 1;
-      if (kt + 1 < KT) gload((kt + 1) * BK);
-      const u16* sp = smem + s * STAGE + (wm * WM + (lane & 31)) * LDS_STRIDE + (lane >> 5) * 8;
-      const u16* sq = smem + s * STAGE + BM * LDS_STRIDE + (wn * WN + (lane & 31)) * LDS_STRIDE +
-                      (lane >> 5) * 8;
+      // This wave's loads of stage kt are done once at most the loads of the
+      // later, already issued stages are outstanding.
+      if (AHEAD >= 3 && kt + 2 < KT) wait_vmcnt<2 * PS>();
+      else if (AHEAD >= 2 && kt + 1 < KT) wait_vmcnt<PS>();
+      else wait_vmcnt<0>();
+      // After the barrier every wave's stage kt is in LDS, and every wave is
+      // done reading stage kt-1, which the next issue overwrites.
+      __syncthreads();
+      if (kt + AHEAD < KT) issue(kt + AHEAD);
+      const unsigned char* stp = sb + (kt % STAGES) * STAGE_BYTES + (wm * WM + r32) * ROW;
+      const unsigned char* stq = sb + (kt % STAGES) * STAGE_BYTES + OP_BYTES + (wn * WN + r32) * ROW;
 #pragma unroll
       for (int kk = 0; kk < BK / 16; ++kk) {
+        const int fo = (((2 * kk) | h) ^ sw) * 16;
         bf16x8 fp[FM], fq[FN];
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
-          fp[i] = *reinterpret_cast<const bf16x8*>(sp + i * 32 * LDS_STRIDE + kk * 16);
+        for (int i = 0; i < FM; ++i) fp[i] = *reinterpret_cast<const bf16x8*>(stp + i * 32 * ROW + fo);
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-          fq[j] = *reinterpret_cast<const bf16x8*>(sq + j * 32 * LDS_STRIDE + kk * 16);
+        for (int j = 0; j < FN; ++j) fq[j] = *reinterpret_cast<const bf16x8*>(stq + j * 32 * ROW + fo);
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
           for (int j = 0; j < FN; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp[i], fq[j], acc[i][j], 0, 0, 0);
       }
-      // One barrier per K step: stage s^1 was last read in step kt-1, which
-      // ended with a barrier, so writing it now is safe.
-      if (kt + 1 < KT) sstore(s ^ 1);
-      __syncthreads();
     }
+    // Every wave is done with the ring before the next tile's first loads.
+    __syncthreads();
   }
 };
 
@@ -180,12 +258,12 @@ struct EngineF32 {
   static constexpr int LDS_STRIDE = BK + 1;  // floats; odd stride spreads rows over banks
   static constexpr int STAGE = (BM + BN) * LDS_STRIDE;
   static constexpr int LDS_BYTES = 2 * STAGE * 4;
-  static __device__ __forceinline__ int wave_m(int w) { return w >> 1; }
-  static __device__ __forceinline__ int wave_n(int w) { return w & 1; }
+  static constexpr bool kStageTile = false;
+  static MUON_INLINE int wave_m(int w) { return w >> 1; }
+  static MUON_INLINE int wave_n(int w) { return w & 1; }
 
-  static __device__ __forceinline__ void run(const float* __restrict__ P, int64_t ldp,
-                                             const float* __restrict__ Q, int64_t ldq, int K,
-                                             float* smem, f32x16 (&acc)[FM][FN]) {
+  static MUON_INLINE void run(const float* __restrict__ P, int64_t ldp, const float* __restrict__ Q,
+                              int64_t ldq, int K, float* smem, f32x16 (&acc)[FM][FN]) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave_m(wave), wn = wave_n(wave);
 #pragma unroll
@@ -195,16 +273,16 @@ struct EngineF32 {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    float4 rp[4], rq[4];
-    auto gload = [&](int k0) {
+    u32x4 rp[4], rq[4];
+    auto gload = [&](int k0) __attribute__((always_inline)) {
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         const int q = tid + p * NT, row = q >> 3, ch = q & 7;
-        rp[p] = *reinterpret_cast<const float4*>(P + row * ldp + k0 + ch * 4);
-        rq[p] = *reinterpret_cast<const float4*>(Q + row * ldq + k0 + ch * 4);
+        rp[p] = gload16(P + row * ldp + k0 + ch * 4);
+        rq[p] = gload16(Q + row * ldq + k0 + ch * 4);
       }
     };
-    auto sstore = [&](int s) {
+    auto sstore = [&](int s) __attribute__((always_inline)) {
       float* sp = smem + s * STAGE;
       float* sq = sp + BM * LDS_STRIDE;
 #pragma unroll
@@ -212,8 +290,11 @@ struct EngineF32 {
         const int q = tid + p * NT, row = q >> 3, ch = q & 7;
         float* dp = sp + row * LDS_STRIDE + ch * 4;
         float* dq = sq + row * LDS_STRIDE + ch * 4;
-        dp[0] = rp[p].x; dp[1] = rp[p].y; dp[2] = rp[p].z; dp[3] = rp[p].w;
-        dq[0] = rq[p].x; dq[1] = rq[p].y; dq[2] = rq[p].z; dq[3] = rq[p].w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          dp[e] = __uint_as_float(rp[p][e]);
+          dq[e] = __uint_as_float(rq[p][e]);
+        }
       }
     };
 
@@ -246,6 +327,31 @@ struct EngineF32 {
   }
 };
 
+// Copies the 256 x 256 bf16 tile at G (row stride ld elements) into LDS, row
+// major with 512-byte rows, in one burst of DMA loads (16 per wave for 8
+// waves), then waits for it. An epilogue that reads an operand tile
+// element by element thus pays one memory latency per tile, not one per
+// accumulator group. The caller has synchronised the workgroup before (the
+// GEMM ring is free) and synchronises it again after its last LDS read.
+template <int NT>
+MUON_INLINE void stage_tile_bf16(const u16* G, int64_t ld, u16* smem) {
+  constexpr int NW = NT / 64, PER_WAVE = 128 / NW;  // 128 KB = 128 wave instructions
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t base = (uint32_t)(uintptr_t)smem;
+#pragma unroll
+  for (int p = 0; p < PER_WAVE; ++p) {
+    const int ins = wave * PER_WAVE + p;             // two rows of 512 bytes each
+    const int row = ins * 2 + (lane >> 5), ch = lane & 31;
+    dma16(G + row * ld + ch * 8, __builtin_amdgcn_readfirstlane(base + ins * 1024));
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+}
+
+MUON_INLINE float lds_tile_bf16(const u16* smem, int64_t r, int64_t c) {
+  return bf16_to_f32(smem[r * 256 + c]);
+}
+
 // ------------------------------------------------------------ phase epilogues
 //
 // Every epilogue walks the accumulators in groups of four consecutive rows of
@@ -256,7 +362,7 @@ template <class E>
 struct TileWalk {
   // Calls f(row0, col, v[4]) for every 4-row group of the tile at (tile_r, tile_c).
   template <class F>
-  static __device__ __forceinline__ void each(int64_t tile_r, int64_t tile_c,
+  static MUON_INLINE void each(int64_t tile_r, int64_t tile_c,
                                               f32x16 (&acc)[E::FM][E::FN], F&& f) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t wr = tile_r + E::wave_m(wave) * E::WM + 4 * (lane >> 5);
@@ -277,7 +383,7 @@ struct TileWalk {
 // Stores a symmetric m x m result tile: C[row][col] and the mirror C[col][row]
 // (off-diagonal tiles only). Entries outside the valid m x m block are 0.
 template <class T>
-__device__ __forceinline__ void store_sym(T* C, int64_t ld, int m, bool mirror, int64_t row0,
+MUON_INLINE void store_sym(T* C, int64_t ld, int m, bool mirror, int64_t row0,
                                           int64_t col, float v[4]) {
   const bool cok = col < m;
 #pragma unroll
@@ -289,7 +395,7 @@ __device__ __forceinline__ void store_sym(T* C, int64_t ld, int m, bool mirror, 
 }
 
 template <class E>
-__device__ void gram_tile(const PhaseArgs& args, const MatDev& d, int ti, int tj, void* smem) {
+MUON_INLINE void gram_tile(const PhaseArgs& args, const MatDev& d, int ti, int tj, void* smem) {
   typedef typename E::T T;
   const T* X = static_cast<const T*>(d.x[args.src]);
   f32x16 acc[E::FM][E::FN];
@@ -304,14 +410,14 @@ __device__ void gram_tile(const PhaseArgs& args, const MatDev& d, int ti, int tj
   T* A = static_cast<T*>(d.a);
   const bool mirror = ti != tj;
   TileWalk<E>::each((int64_t)ti * E::BM, (int64_t)tj * E::BN, acc,
-                    [&](int64_t row0, int64_t col, float v[4]) {
+                    [&](int64_t row0, int64_t col, float v[4]) __attribute__((always_inline)) {
                       for (int q = 0; q < 4; ++q) v[q] *= alpha;
                       store_sym<T>(A, d.mp, d.m, mirror, row0, col, v);
                     });
 }
 
 template <class E>
-__device__ void square_tile(const PhaseArgs& args, const MatDev& d, int ti, int tj, void* smem) {
+MUON_INLINE void square_tile(const PhaseArgs& args, const MatDev& d, int ti, int tj, void* smem) {
   typedef typename E::T T;
   const T* A = static_cast<const T*>(d.a);
   f32x16 acc[E::FM][E::FN];
@@ -320,17 +426,26 @@ __device__ void square_tile(const PhaseArgs& args, const MatDev& d, int ti, int 
   T* B = static_cast<T*>(d.b);
   const float cb = args.co.b, cc = args.co.c;
   const bool mirror = ti != tj;
-  TileWalk<E>::each((int64_t)ti * E::BM, (int64_t)tj * E::BN, acc,
-                    [&](int64_t row0, int64_t col, float v[4]) {
+  const int64_t tr = (int64_t)ti * E::BM, tc = (int64_t)tj * E::BN;
+  if constexpr (E::kStageTile) stage_tile_bf16<E::NT>(A + tr * d.mp + tc, d.mp, static_cast<T*>(smem));
+  TileWalk<E>::each(tr, tc, acc,
+                    [&](int64_t row0, int64_t col, float v[4]) __attribute__((always_inline)) {
                       // B = b*A + c*(A*A), formed in fp32 and rounded once.
-                      for (int q = 0; q < 4; ++q)
-                        v[q] = cb * Elem<T>::load(A + (row0 + q) * d.mp + col) + cc * v[q];
+                      for (int q = 0; q < 4; ++q) {
+                        float aij;
+                        if constexpr (E::kStageTile)
+                          aij = lds_tile_bf16(static_cast<const u16*>(smem), row0 + q - tr, col - tc);
+                        else
+                          aij = Elem<T>::load(A + (row0 + q) * d.mp + col);
+                        v[q] = cb * aij + cc * v[q];
+                      }
                       store_sym<T>(B, d.mp, d.m, mirror, row0, col, v);
                     });
+  if constexpr (E::kStageTile) __syncthreads();
 }
 
 template <class E>
-__device__ void update_tile(const PhaseArgs& args, const MatDev& d, int ti, int tj, void* smem) {
+MUON_INLINE void update_tile(const PhaseArgs& args, const MatDev& d, int ti, int tj, void* smem) {
   typedef typename E::T T;
   const int src = args.src, dst = src ^ 1;
   const T* B = static_cast<const T*>(d.b);
@@ -345,41 +460,48 @@ __device__ void update_tile(const PhaseArgs& args, const MatDev& d, int ti, int 
   // X1 = s * (a U + B U).
   const float xs = args.first ? args.scale[&d - args.mats] : 1.f;
   const int m = d.m, n = d.n;
+  const int64_t tr = (int64_t)ti * E::BM, tc = (int64_t)tj * E::BN;
+  if constexpr (E::kStageTile) stage_tile_bf16<E::NT>(X + tr * d.np + tc, d.np, static_cast<T*>(smem));
+  auto xval = [&](int64_t r, int64_t c) __attribute__((always_inline)) -> float {
+    if constexpr (E::kStageTile) return lds_tile_bf16(static_cast<const u16*>(smem), r - tr, c - tc);
+    else return Elem<T>::load(X + r * d.np + c);
+  };
   if (!args.last) {
     T* Xo = static_cast<T*>(d.x[dst]);
     T* Xto = static_cast<T*>(d.xt[dst]);
-    TileWalk<E>::each((int64_t)ti * E::BM, (int64_t)tj * E::BN, acc,
-                      [&](int64_t row0, int64_t col, float v[4]) {
+    TileWalk<E>::each(tr, tc, acc,
+                      [&](int64_t row0, int64_t col, float v[4]) __attribute__((always_inline)) {
                         const bool cok = col < n;
 #pragma unroll
                         for (int q = 0; q < 4; ++q) {
                           const int64_t o = (row0 + q) * d.np + col;
-                          v[q] = (cok && row0 + q < m) ? xs * (ca * Elem<T>::load(X + o) + v[q]) : 0.f;
+                          v[q] = (cok && row0 + q < m) ? xs * (ca * xval(row0 + q, col) + v[q]) : 0.f;
                           Elem<T>::store(Xo + o, v[q]);
                         }
                         Vec4<T>::store(Xto + col * d.mp + row0, v);
                       });
-    return;
-  }
-  // Last iteration: O = X_T (or X_T^T for a tall matrix).
-  // W -= lr*scale*O, delta = -lr*scale*O.
-  T* W = static_cast<T*>(d.w);
-  T* D = static_cast<T*>(d.delta);
-  const float ls = d.lr_scale;
-  const int64_t ldw = d.cols;
-  TileWalk<E>::each((int64_t)ti * E::BM, (int64_t)tj * E::BN, acc,
-                    [&](int64_t row0, int64_t col, float v[4]) {
-                      if (col >= n) return;
+  } else {
+    // Last iteration: O = X_T (or X_T^T for a tall matrix).
+    // W -= lr*scale*O, delta = -lr*scale*O.
+    T* W = static_cast<T*>(d.w);
+    T* D = static_cast<T*>(d.delta);
+    const float ls = d.lr_scale;
+    const int64_t ldw = d.cols;
+    TileWalk<E>::each(tr, tc, acc,
+                      [&](int64_t row0, int64_t col, float v[4]) __attribute__((always_inline)) {
+                        if (col >= n) return;
 #pragma unroll
-                      for (int q = 0; q < 4; ++q) {
-                        const int64_t r = row0 + q;
-                        if (r >= m) break;
-                        const float o = xs * (ca * Elem<T>::load(X + r * d.np + col) + v[q]);
-                        const int64_t wo = d.tall ? col * ldw + r : r * ldw + col;
-                        if (W) Elem<T>::store(W + wo, Elem<T>::load(W + wo) - ls * o);
-                        if (D) Elem<T>::store(D + wo, -ls * o);
-                      }
-                    });
+                        for (int q = 0; q < 4; ++q) {
+                          const int64_t r = row0 + q;
+                          if (r >= m) break;
+                          const float o = xs * (ca * xval(r, col) + v[q]);
+                          const int64_t wo = d.tall ? col * ldw + r : r * ldw + col;
+                          if (W) Elem<T>::store(W + wo, Elem<T>::load(W + wo) - ls * o);
+                          if (D) Elem<T>::store(D + wo, -ls * o);
+                        }
+                      });
+  }
+  if constexpr (E::kStageTile) __syncthreads();
 }
 
 // ------------------------------------------------------------ persistent phase kernel
@@ -388,27 +510,30 @@ template <class E, int PH>
 __global__ void __launch_bounds__(E::NT) phase_kernel(PhaseArgs args) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[E::LDS_BYTES];
   __shared__ int s_tile;
-  if (threadIdx.x == 0) s_tile = atomicAdd(args.counter, 1);
-  __syncthreads();
-  int t = s_tile;
-  while (t < args.n_tiles) {
-    const Tile tile = args.tiles[t];
-    const MatDev& d = args.mats[tile.mat];
-    const int ti = tile.ij >> 16, tj = tile.ij & 0xffff;
-    if (PH == kGram) gram_tile<E>(args, d, ti, tj, smem);
-    else if (PH == kSquare) square_tile<E>(args, d, ti, tj, smem);
-    else update_tile<E>(args, d, ti, tj, smem);
-    __syncthreads();  // every thread has read s_tile and finished with LDS
-    if (threadIdx.x == 0) s_tile = atomicAdd(args.counter, 1);
-    __syncthreads();
-    t = s_tile;
+  const int home = blockIdx.x % kQueues;
+  for (int qq = 0; qq < kQueues; ++qq) {
+    const int q = (home + qq) % kQueues;
+    const int base = args.qoff[q], len = args.qoff[q + 1] - base;
+    while (true) {
+      if (threadIdx.x == 0) s_tile = atomicAdd(args.counter + q, 1);
+      __syncthreads();
+      const int t = s_tile;
+      __syncthreads();  // every thread has read s_tile before thread 0 writes it again
+      if (t >= len) break;
+      const Tile tile = args.tiles[base + t];
+      const MatDev& d = args.mats[tile.mat];
+      const int ti = tile.ij >> 16, tj = tile.ij & 0xffff;
+      if (PH == kGram) gram_tile<E>(args, d, ti, tj, smem);
+      else if (PH == kSquare) square_tile<E>(args, d, ti, tj, smem);
+      else update_tile<E>(args, d, ti, tj, smem);
+    }
   }
 }
 
 // ------------------------------------------------------------ elementwise kernels
 
 // Matrix of elementwise block b: the last i with prefix[i] <= b.
-__device__ __forceinline__ int find_mat(const int32_t* prefix, int n, int b) {
+MUON_INLINE int find_mat(const int32_t* prefix, int n, int b) {
   int lo = 0, hi = n - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -417,7 +542,7 @@ __device__ __forceinline__ int find_mat(const int32_t* prefix, int n, int b) {
   return lo;
 }
 
-__device__ __forceinline__ float block_sum_256(float v, float* red) {
+MUON_INLINE float block_sum_256(float v, float* red) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
@@ -488,9 +613,7 @@ __global__ void __launch_bounds__(256) momentum_kernel(EwArgs args) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       ss += u[e] * u[e];
-      T tv;
-      Elem<T>::store(&tv, u[e]);
-      tileU[lr][lc + e] = tv;
+      tileU[lr][lc + e] = Elem<T>::to_storage(u[e]);
     }
   }
   const float tot = block_sum_256(ss, red);  // contains a barrier: tileU is complete
@@ -506,10 +629,10 @@ __global__ void __launch_bounds__(256) momentum_kernel(EwArgs args) {
     if (gr + 3 < rows) {
       float v[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = Elem<T>::load(&tileU[lr + e][lc]);
+      for (int e = 0; e < 4; ++e) v[e] = Elem<T>::lds_load(&tileU[lr + e][lc]);
       Vec4<T>::store(dst, v);
     } else {
-      for (int e = 0; e < 4 && gr + e < rows; ++e) dst[e] = tileU[lr + e][lc];
+      for (int e = 0; e < 4 && gr + e < rows; ++e) Elem<T>::store(dst + e, Elem<T>::lds_load(&tileU[lr + e][lc]));
     }
   }
 }
@@ -584,14 +707,17 @@ static hipError_t launch_phase_e(Phase ph, const PhaseArgs& args, int32_t grid, 
   return hipGetLastError();
 }
 
-hipError_t launch_phase(int dtype, Phase ph, const PhaseArgs& args, int32_t grid, hipStream_t s) {
-  return dtype == 1 ? launch_phase_e<EngineBF16>(ph, args, grid, s)
-                    : launch_phase_e<EngineF32>(ph, args, grid, s);
+hipError_t launch_phase(int dtype, int variant, Phase ph, const PhaseArgs& args, int32_t grid,
+                        hipStream_t s) {
+  if (dtype != 1) return launch_phase_e<EngineF32>(ph, args, grid, s);
+  if (variant == kGemmBK32) return launch_phase_e<EngineBF16<2, 4, 32, 4>>(ph, args, grid, s);
+  return launch_phase_e<EngineBF16<2, 4, 64, 2>>(ph, args, grid, s);
 }
 
-int gemm_blocks_per_cu(int dtype) {
-  // 147 KB of LDS per bf16 workgroup: one per CU. The fp32 engine uses
-  // 66 KB and 256 threads: two per CU.
+int gemm_blocks_per_cu(int dtype, int variant) {
+  // Each bf16 workgroup holds 128 KB of LDS: one per CU. The fp32 engine
+  // uses 66 KB and 256 threads: two per CU.
+  (void)variant;
   return dtype == 1 ? 1 : 2;
 }
 
