@@ -51,7 +51,8 @@ def parse():
     ap.add_argument("--cpu-sample", default="1,2,0,3",
                     help="matrix indices the oracle times for the CPU baseline")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
-                    help="also run one plain torch copy of this many MiB (HBM counter scaling)")
+                    help="also run one plain elementwise copy kernel (torch.add, fp32) over this "
+                         "many MiB, the reference for scaling HBM byte counters")
     return ap.parse_args()
 
 
@@ -91,6 +92,33 @@ def cpu_baseline(wload, indices):
             "kind": "oracle", "seconds": round(dt, 3),
             "sample": f"fp64 numpy oracle, full step on {len(indices)} of {len(wload.shapes)} "
                       f"matrices ({', '.join(shapes)}) of the same workload"}
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "update_kernel_traffic_qwen3_32b_layer.txt")
+KERNEL_SOURCE = os.path.join(ROOT, "matrix_optimizer_step_muon_amd", "csrc", "muon_kernels.hip")
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def committed_traffic(workload: str):
+    """HBM bytes per update launch from the committed rocprofv3 counter summary.
+
+    FETCH_SIZE and WRITE_SIZE of the update kernel, each scaled by what the same
+    counter reads for a plain copy kernel of known size. The value is used only
+    if the counters were taken on this exact kernel source and workload, and
+    is None otherwise."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256") != kernel_source_hash() or t.get("workload") != workload:
+        return None
+    return t.get("hbm_bytes_per_launch")
 
 
 def main():
@@ -158,7 +186,7 @@ def main():
         src = torch.empty(n, dtype=torch.float32, device="cuda").uniform_()
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
-        dst.copy_(src)
+        torch.add(src, 1.0, out=dst)   # one kernel: reads and writes copy_probe_mib MiB
         torch.cuda.synchronize()
         del src, dst
 
@@ -201,7 +229,8 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(upd_tflops / peak, 4) if upd_tflops else None,
-            "traffic": None,
+            "traffic": committed_traffic(args.workload),
+            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-scaled)",
             "alg_tflop_per_launch": round(fl["update"] / 1e12, 4),
             "avg_launch_ms": round(upd_avg, 4),
         },

@@ -202,12 +202,20 @@ muon_status muon_plan(const muon_matrix* mats, int32_t n, const muon_hparams* hp
     d.delta = s.delta;
     d.g = s.g;
     d.mom = s.m;
-    const size_t xbytes = size_t(d.mp) * d.np * p->elem;
-    const size_t abytes = size_t(d.mp) * d.mp * p->elem;
+    // Row strides are one 128-byte line longer than the padded width. All
+    // padded widths are multiples of 16 lines, and without the skew the rows
+    // of a tile would fall on the same L2 channel.
+    const int32_t skew = int32_t(128 / p->elem);
+    d.ldx = d.np + skew;
+    d.ldt = d.mp + skew;
+    d.lda = d.mp + skew;
+    const size_t xbytes = size_t(d.mp) * d.ldx * p->elem;
+    const size_t tbytes = size_t(d.np) * d.ldt * p->elem;
+    const size_t abytes = size_t(d.mp) * d.lda * p->elem;
     off[i * 6 + 0] = take(xbytes);
     off[i * 6 + 1] = take(xbytes);
-    off[i * 6 + 2] = take(xbytes);
-    off[i * 6 + 3] = take(xbytes);
+    off[i * 6 + 2] = take(tbytes);
+    off[i * 6 + 3] = take(tbytes);
     off[i * 6 + 4] = take(abytes);
     off[i * 6 + 5] = take(abytes);
   }
@@ -227,22 +235,34 @@ muon_status muon_plan(const muon_matrix* mats, int32_t n, const muon_hparams* hp
   // and a block's tiles stay in row-major order.
   struct Block { int64_t cost; std::vector<muon::Tile> tiles; };
   std::vector<Block> blocks[3];
+  // Blocks are walked column-major: consecutive blocks, dealt to different
+  // XCDs, share the column operand's panels in the Infinity Cache. Tuning
+  // knobs: MUON_BLOCK=RxC sets the block shape in tiles, and
+  // MUON_BLOCK_ORDER=0 walks blocks row-major instead.
+  int brows = muon::kBlockRows, bcols = muon::kBlockCols, border = 1;
+  if (const char* v = std::getenv("MUON_BLOCK")) {
+    int r = 0, c = 0;
+    if (std::sscanf(v, "%dx%d", &r, &c) == 2 && r > 0 && c > 0 && r * c <= 1024) { brows = r; bcols = c; }
+  }
+  if (const char* v = std::getenv("MUON_BLOCK_ORDER")) border = std::atoi(v) != 0;
   for (int32_t i = 0; i < n; ++i) {
     const muon::MatDev& d = p->mats[i];
     const int32_t tm = int32_t(d.mp / T), tn = int32_t(d.np / T);
     for (int ph = 0; ph < 3; ++ph) {
       const int32_t cols = ph == muon::kUpdate ? tn : tm;
       const int64_t K = ph == muon::kGram ? d.np : d.mp;
-      for (int32_t r0 = 0; r0 < tm; r0 += muon::kBlockRows)
-        for (int32_t c0 = 0; c0 < cols; c0 += muon::kBlockCols) {
-          Block b{0, {}};
-          for (int32_t a = r0; a < std::min(tm, r0 + muon::kBlockRows); ++a)
-            for (int32_t c = c0; c < std::min(cols, c0 + muon::kBlockCols); ++c)
-              if (ph == muon::kUpdate || c >= a) b.tiles.push_back({i, (a << 16) | c});
-          if (b.tiles.empty()) continue;
-          b.cost = int64_t(b.tiles.size()) * K;
-          blocks[ph].push_back(std::move(b));
-        }
+      const int32_t nbr = (tm + brows - 1) / brows, nbc = (cols + bcols - 1) / bcols;
+      for (int32_t bi = 0; bi < nbr * nbc; ++bi) {
+        const int32_t r0 = (border ? bi % nbr : bi / nbc) * brows;
+        const int32_t c0 = (border ? bi / nbr : bi % nbc) * bcols;
+        Block b{0, {}};
+        for (int32_t a = r0; a < std::min(tm, r0 + brows); ++a)
+          for (int32_t c = c0; c < std::min(cols, c0 + bcols); ++c)
+            if (ph == muon::kUpdate || c >= a) b.tiles.push_back({i, (a << 16) | c});
+        if (b.tiles.empty()) continue;
+        b.cost = int64_t(b.tiles.size()) * K;
+        blocks[ph].push_back(std::move(b));
+      }
     }
   }
   size_t o_tiles[3];

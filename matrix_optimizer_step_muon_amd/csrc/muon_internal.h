@@ -26,10 +26,10 @@ constexpr int kBlockCols = 8;
 // One matrix of the batch as the kernels see it. X is the m x n orientation
 // of U (m = min(rows, cols)): U itself, or U^T when rows > cols.
 struct MatDev {
-  void* x[2];         // X ping/pong: mp x np, row-major, ld = np
-  void* xt[2];        // X^T ping/pong: np x mp, row-major, ld = mp
-  void* a;            // A = X X^T: mp x mp
-  void* b;            // B = b*A + c*A*A: mp x mp
+  void* x[2];         // X ping/pong: mp x np, row-major, leading dimension ldx
+  void* xt[2];        // X^T ping/pong: np x mp, row-major, leading dimension ldt
+  void* a;            // A = X X^T: mp x mp, leading dimension lda
+  void* b;            // B = b*A + c*A*A: mp x mp, leading dimension lda
   void* w;            // weights rows x cols (may be null)
   void* delta;        // Delta W rows x cols (may be null)
   const void* g;      // gradient rows x cols
@@ -37,12 +37,14 @@ struct MatDev {
   int32_t rows, cols;
   int32_t m, n;       // m = min(rows, cols), n = max(rows, cols)
   int32_t mp, np;     // m, n rounded up to the GEMM tile edge
+  int32_t ldx, ldt, lda;  // row strides (elements) of X, X^T and A/B: the padded
+                          // width plus one 128-byte line, so the rows of a tile
+                          // spread over all L2 channels
   int32_t tall;       // rows > cols
   int32_t ew_tiles_c; // elementwise tiles along cols: ceil(cols / 64)
   int32_t part_off;   // first norm-partial slot of this matrix
   int32_t n_parts;    // number of elementwise tiles (= partial slots)
   float lr_scale;     // lr * sqrt(max(1, rows / cols))
-  float pad_;
 };
 
 // One output tile of a GEMM phase: matrix index and tile coordinates.
@@ -58,7 +60,9 @@ struct StepCoeffs {
   int32_t nesterov;
 };
 
-enum Phase { kGram = 0, kSquare = 1, kUpdate = 2 };
+// Kernel phases. kUpdateLast is the last iteration's update, which applies the
+// step to W (and delta) instead of storing X; it uses the update tile tables.
+enum Phase { kGram = 0, kSquare = 1, kUpdate = 2, kUpdateLast = 3 };
 
 // Arguments of one persistent GEMM-phase launch.
 struct PhaseArgs {

@@ -167,14 +167,20 @@ struct EngineBF16 {
   static constexpr int RPI = 1024 / ROW;            // rows per DMA wave instruction
   static constexpr int OP_BYTES = BM * ROW;         // one operand tile of one stage
   static constexpr int STAGE_BYTES = 2 * OP_BYTES;  // P and Q
-  static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
   static constexpr int DPW = OP_BYTES / 1024 / NW;  // DMA instructions per wave per operand
+  static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
   static constexpr bool kStageTile = true;          // epilogue operand tiles go through LDS
   static MUON_INLINE int wave_m(int w) { return w / WAVES_N; }
   static MUON_INLINE int wave_n(int w) { return w % WAVES_N; }
 
+  // diag_kt0 >= 0 (update phase only): the Q operand is the X^T panel of the
+  // output tile's columns, and its K steps diag_kt0 .. diag_kt0 + BM/BK - 1
+  // hold X^T over the tile's own rows. While those steps are in LDS, the waves
+  // that own the matching output rows add diag_coef * X[r][c] to their
+  // accumulators, so the a*X term of X' = a*X + B*X needs no separate read of X.
   static MUON_INLINE void run(const u16* __restrict__ P, int64_t ldp, const u16* __restrict__ Q,
-                              int64_t ldq, int K, u16* smem, f32x16 (&acc)[FM][FN]) {
+                              int64_t ldq, int K, u16* smem, f32x16 (&acc)[FM][FN],
+                              int diag_kt0 = -1, float diag_coef = 0.f) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave_m(wave), wn = wave_n(wave);
 #pragma unroll
@@ -206,45 +212,108 @@ struct EngineBF16 {
         dma16(gq[p] + kt * BK, __builtin_amdgcn_readfirstlane(st + OP_BYTES + off));
       }
     };
-
     // Fragment reads: lane l reads row l % 32 of each 32-row block, 16-byte
     // chunk 2*kk + l/32, at slot chunk ^ swz(row).
     const int r32 = lane & 31, h = lane >> 5, sw = lds_swizzle<S>(r32);
     const unsigned char* sb = reinterpret_cast<const unsigned char*>(smem);
+    const uint32_t rowp = (wm * WM + r32) * ROW, rowq = OP_BYTES + (wn * WN + r32) * ROW;
 
-    const int KT = K / BK;
-    constexpr int AHEAD = STAGES - 1;
-    constexpr int PS = 2 * DPW;  // DMA instructions per wave per stage
+    // Register fragments are double-buffered: the reads of sub-step kk+1 are
+    // in flight while the MFMAs of sub-step kk run.
+    constexpr int KK = BK / 16;
+    bf16x8 fp[2][FM], fq[2][FN];
+    auto read_frags = [&](int buf, int kt, int kk) __attribute__((always_inline)) {
+      const unsigned char* st = sb + (kt % STAGES) * STAGE_BYTES;
+      const int fo = (((2 * kk) | h) ^ sw) * 16;
 #pragma unroll
-    for (int k = 0; k < AHEAD; ++k)
-      if (k < KT) issue(k);
-    for (int kt = 0; kt < KT; ++kt) {
-      // This wave's loads of stage kt are done once at most the loads of the
-      // later, already issued stages are outstanding.
-      if (AHEAD >= 3 && kt + 2 < KT) wait_vmcnt<2 * PS>();
-      else if (AHEAD >= 2 && kt + 1 < KT) wait_vmcnt<PS>();
-      else wait_vmcnt<0>();
-      // After the barrier every wave's stage kt is in LDS, and every wave is
-      // done reading stage kt-1, which the next issue overwrites.
-      __syncthreads();
-      if (kt + AHEAD < KT) issue(kt + AHEAD);
-      const unsigned char* stp = sb + (kt % STAGES) * STAGE_BYTES + (wm * WM + r32) * ROW;
-      const unsigned char* stq = sb + (kt % STAGES) * STAGE_BYTES + OP_BYTES + (wn * WN + r32) * ROW;
+      for (int i = 0; i < FM; ++i) fp[buf][i] = *reinterpret_cast<const bf16x8*>(st + rowp + i * 32 * ROW + fo);
 #pragma unroll
-      for (int kk = 0; kk < BK / 16; ++kk) {
-        const int fo = (((2 * kk) | h) ^ sw) * 16;
-        bf16x8 fp[FM], fq[FN];
+      for (int j = 0; j < FN; ++j) fq[buf][j] = *reinterpret_cast<const bf16x8*>(st + rowq + j * 32 * ROW + fo);
+    };
+    auto mfmas = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < FM; ++i) fp[i] = *reinterpret_cast<const bf16x8*>(stp + i * 32 * ROW + fo);
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) fq[j] = *reinterpret_cast<const bf16x8*>(stq + j * 32 * ROW + fo);
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp[buf][i], fq[buf][j], acc[i][j], 0, 0, 0);
+    };
+    // K step kt of the diagonal window covers tile rows slab*BK .. +BK, with
+    // slab = kt - diag_kt0. Accumulator group (i, j, g) of this lane holds
+    // rows R .. R+3, R = wm*WM + 32i + 8g + 4(l/32), of column
+    // c = wn*WN + 32j + l%32. X[R + q][c] sits in Q-stage row c at k offset
+    // R + q - slab*BK: 4 consecutive bf16, one 8-byte LDS read.
+    auto diag_add = [&](int kt) __attribute__((always_inline)) {
+      const int slab = kt - diag_kt0;
+      if (diag_kt0 < 0 || slab < 0 || slab >= BM / BK) return;
+      const unsigned char* st = sb + (kt % STAGES) * STAGE_BYTES + OP_BYTES;
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+      for (int i = 0; i < FM; ++i) {
+        const int rbase = wm * WM + i * 32 + 4 * h - slab * BK;  // k offset of row R for g = 0
+        if (rbase + 28 < 0 || rbase >= BK) continue;              // block outside this slab
 #pragma unroll
-          for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp[i], fq[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < FN; ++j) {
+          const int c = wn * WN + j * 32 + r32;
+          const unsigned char* rowc = st + c * ROW;
+          const int swc = lds_swizzle<S>(c);
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int ko = rbase + 8 * g;
+            if (ko < 0 || ko >= BK) continue;
+            const u32x2 v = *reinterpret_cast<const u32x2*>(rowc + (((ko >> 3) ^ swc) << 4) + (ko & 7) * 2);
+            acc[i][j][4 * g + 0] += diag_coef * __uint_as_float(v[0] << 16);
+            acc[i][j][4 * g + 1] += diag_coef * __uint_as_float(v[0] & 0xffff0000u);
+            acc[i][j][4 * g + 2] += diag_coef * __uint_as_float(v[1] << 16);
+            acc[i][j][4 * g + 3] += diag_coef * __uint_as_float(v[1] & 0xffff0000u);
+          }
+        }
       }
+    };
+    const int KT = K / BK;
+    constexpr int PS = 2 * DPW;  // DMA instructions per wave per stage
+    // Waits until this wave's loads of stage j are done: at most the loads of
+    // the later stages already issued, min(STAGES - 2, KT - 1 - j) of them,
+    // may still be outstanding.
+    auto wait_stage = [&](int j) __attribute__((always_inline)) {
+      const int later = KT - 1 - j;
+      if (STAGES >= 4 && later >= 2) wait_vmcnt<2 * PS>();
+      else if (STAGES >= 3 && later >= 1) wait_vmcnt<PS>();
+      else wait_vmcnt<0>();
+    };
+
+#pragma unroll
+    for (int k = 0; k < STAGES - 1; ++k)
+      if (k < KT) issue(k);
+    wait_stage(0);
+    __syncthreads();
+    if (STAGES - 1 < KT) issue(STAGES - 1);
+    read_frags(0, 0, 0);
+    for (int kt = 0; kt < KT - 1; ++kt) {
+      diag_add(kt);
+#pragma unroll
+      for (int kk = 0; kk < KK - 1; ++kk) {
+        read_frags((kk + 1) & 1, kt, kk + 1);
+        mfmas(kk & 1);
+      }
+      // The last sub-step's MFMAs are issued before the wait and the barrier,
+      // so they keep the matrix pipe busy across both, the next DMA issue and
+      // the first fragment reads of stage kt+1.
+      mfmas((KK - 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+      wait_stage(kt + 1);
+      // After the barrier, every wave's stage kt+1 is in LDS, and every wave
+      // is done reading stage kt, which the next issue overwrites.
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+      if (kt + STAGES < KT) issue(kt + STAGES);
+      read_frags(0, kt + 1, 0);
     }
+    diag_add(KT - 1);
+#pragma unroll
+    for (int kk = 0; kk < KK - 1; ++kk) {
+      read_frags((kk + 1) & 1, KT - 1, kk + 1);
+      mfmas(kk & 1);
+    }
+    mfmas((KK - 1) & 1);
     // Every wave is done with the ring before the next tile's first loads.
     __syncthreads();
   }
@@ -263,7 +332,7 @@ struct EngineF32 {
   static MUON_INLINE int wave_n(int w) { return w & 1; }
 
   static MUON_INLINE void run(const float* __restrict__ P, int64_t ldp, const float* __restrict__ Q,
-                              int64_t ldq, int K, float* smem, f32x16 (&acc)[FM][FN]) {
+                              int64_t ldq, int K, float* smem, f32x16 (&acc)[FM][FN], int = -1, float = 0.f) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave_m(wave), wn = wave_n(wave);
 #pragma unroll
@@ -355,15 +424,20 @@ MUON_INLINE float lds_tile_bf16(const u16* smem, int64_t r, int64_t c) {
 // ------------------------------------------------------------ phase epilogues
 //
 // Every epilogue walks the accumulators in groups of four consecutive rows of
-// one column: rows row0..row0+3 of column col. A mirrored (transposed) copy of
-// such a group is one contiguous 4-element store.
+// one column: rows row0..row0+3 of column col.
+//
+// bf16 engines (kStageTile): the epilogue computes the output values in place
+// in the accumulators. It then writes them through LDS, once per output
+// orientation. A 256 x 256 bf16 tile goes to LDS (2-byte writes for the
+// normal orientation, 8-byte writes for the transposed one), and then to
+// global memory in coalesced 16-byte stores, a whole 512-byte row per 32
+// lanes. The fp32 engine stores straight from the accumulators.
 
 template <class E>
 struct TileWalk {
   // Calls f(row0, col, v[4]) for every 4-row group of the tile at (tile_r, tile_c).
   template <class F>
-  static MUON_INLINE void each(int64_t tile_r, int64_t tile_c,
-                                              f32x16 (&acc)[E::FM][E::FN], F&& f) {
+  static MUON_INLINE void each(int64_t tile_r, int64_t tile_c, f32x16 (&acc)[E::FM][E::FN], F&& f) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t wr = tile_r + E::wave_m(wave) * E::WM + 4 * (lane >> 5);
     const int64_t wc = tile_c + E::wave_n(wave) * E::WN + (lane & 31);
@@ -378,13 +452,35 @@ struct TileWalk {
           f(wr + i * 32 + 8 * g, wc + j * 32, v);
         }
   }
+  // Same walk; f may change v, and the result goes back into the accumulators.
+  template <class F>
+  static MUON_INLINE void apply(int64_t tile_r, int64_t tile_c, f32x16 (&acc)[E::FM][E::FN], F&& f) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t wr = tile_r + E::wave_m(wave) * E::WM + 4 * (lane >> 5);
+    const int64_t wc = tile_c + E::wave_n(wave) * E::WN + (lane & 31);
+#pragma unroll
+    for (int i = 0; i < E::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < E::FN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                        acc[i][j][4 * g + 3]};
+          f(wr + i * 32 + 8 * g, wc + j * 32, v);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[i][j][4 * g + q] = v[q];
+          // One 32 x 32 block at a time: keeps the compiler from hoisting
+          // every load of the walk ahead of the arithmetic (register spills).
+          if (g == 3) __builtin_amdgcn_sched_barrier(0);
+        }
+  }
 };
 
-// Stores a symmetric m x m result tile: C[row][col] and the mirror C[col][row]
-// (off-diagonal tiles only). Entries outside the valid m x m block are 0.
+// Stores a symmetric m x m result tile straight from the accumulators:
+// C[row][col] and the mirror C[col][row] (off-diagonal tiles only). Entries
+// outside the valid m x m block are 0.
 template <class T>
-MUON_INLINE void store_sym(T* C, int64_t ld, int m, bool mirror, int64_t row0,
-                                          int64_t col, float v[4]) {
+MUON_INLINE void store_sym(T* C, int64_t ld, int m, bool mirror, int64_t row0, int64_t col, float v[4]) {
   const bool cok = col < m;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -394,12 +490,93 @@ MUON_INLINE void store_sym(T* C, int64_t ld, int m, bool mirror, int64_t row0,
   if (mirror) Vec4<T>::store(C + col * ld + row0, v);
 }
 
+// Output staging tile: 256 rows of 256 bf16, padded to 528 bytes so that the
+// two 64-byte halves a wave writes per row group fall on different banks.
+constexpr int kOutStride = 528;
+constexpr int kOutBytes = 256 * kOutStride;
+
+MUON_INLINE uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// Accumulator tile -> LDS staging tile as bf16, in the normal (row r, col c)
+// or the transposed (row c, col r) orientation.
+template <class E>
+MUON_INLINE void acc_to_lds(f32x16 (&acc)[E::FM][E::FN], unsigned char* smem, bool transposed) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wr = E::wave_m(wave) * E::WM + 4 * (lane >> 5);
+  const int wc = E::wave_n(wave) * E::WN + (lane & 31);
+#pragma unroll
+  for (int i = 0; i < E::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < E::FN; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int r0 = wr + i * 32 + 8 * g, c = wc + j * 32;
+        if (transposed) {
+          u32x2 t;
+          t[0] = pack_bf16x2(acc[i][j][4 * g], acc[i][j][4 * g + 1]);
+          t[1] = pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+          *reinterpret_cast<u32x2*>(smem + c * kOutStride + r0 * 2) = t;
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<u16*>(smem + (r0 + q) * kOutStride + c * 2) = f32_to_bf16(acc[i][j][4 * g + q]);
+        }
+      }
+}
+
+// LDS staging tile -> the 256 x 256 tile of a bf16 matrix whose origin is dst
+// (row stride ld elements), in 16-byte stores.
+template <int NT>
+MUON_INLINE void lds_to_global(const unsigned char* smem, u16* dst, int64_t ld) {
+#pragma unroll 2
+  for (int p = 0; p < 256 * 32 / NT; ++p) {
+    const int idx = threadIdx.x + p * NT, row = idx >> 5, ch = idx & 31;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(smem + row * kOutStride + ch * 16);
+    *((g_u32x4*)(dst + row * ld + ch * 8)) = v;
+  }
+}
+
+// LDS staging tile -> the transpose of the tile at dst_t: row c of dst_t gets
+// column c of the staging tile. A lane gathers 8 consecutive rows of one
+// column (2-byte LDS reads; a wave reads 64 adjacent columns of one row at a
+// time) and stores them as one 16-byte chunk.
+template <int NT>
+MUON_INLINE void lds_to_global_t(const unsigned char* smem, u16* dst_t, int64_t ld_t) {
+  const int c = threadIdx.x & 255;
+#pragma unroll 2
+  for (int p = 0; p < 256 * 32 / NT; ++p) {
+    const int r0 = 8 * ((threadIdx.x >> 8) + p * (NT / 256));
+    const unsigned char* col = smem + r0 * kOutStride + c * 2;
+    u32x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      v[e] = (uint32_t)*reinterpret_cast<const u16*>(col + (2 * e) * kOutStride) |
+             ((uint32_t)*reinterpret_cast<const u16*>(col + (2 * e + 1) * kOutStride) << 16);
+    *((g_u32x4*)(dst_t + c * ld_t + r0)) = v;
+  }
+}
+
+// Writes the (masked) accumulator tile to dst and, if dst_t is set, its
+// transpose to dst_t, through one LDS staging pass. LDS must be free on entry;
+// it is free again on exit.
+template <class E>
+MUON_INLINE void store_tile_staged(f32x16 (&acc)[E::FM][E::FN], unsigned char* smem, u16* dst, int64_t ld,
+                                   u16* dst_t, int64_t ld_t) {
+  acc_to_lds<E>(acc, smem, false);
+  __syncthreads();
+  lds_to_global<E::NT>(smem, dst, ld);
+  if (dst_t) lds_to_global_t<E::NT>(smem, dst_t, ld_t);
+  __syncthreads();
+}
+
 template <class E>
 MUON_INLINE void gram_tile(const PhaseArgs& args, const MatDev& d, int ti, int tj, void* smem) {
   typedef typename E::T T;
   const T* X = static_cast<const T*>(d.x[args.src]);
   f32x16 acc[E::FM][E::FN];
-  E::run(X + (int64_t)ti * E::BM * d.np, d.np, X + (int64_t)tj * E::BN * d.np, d.np, d.np,
+  E::run(X + (int64_t)ti * E::BM * d.ldx, d.ldx, X + (int64_t)tj * E::BN * d.ldx, d.ldx, d.np,
          static_cast<T*>(smem), acc);
   // First iteration: X holds the unscaled U, so A = s^2 U U^T.
   float alpha = 1.f;
@@ -409,11 +586,20 @@ MUON_INLINE void gram_tile(const PhaseArgs& args, const MatDev& d, int ti, int t
   }
   T* A = static_cast<T*>(d.a);
   const bool mirror = ti != tj;
-  TileWalk<E>::each((int64_t)ti * E::BM, (int64_t)tj * E::BN, acc,
-                    [&](int64_t row0, int64_t col, float v[4]) __attribute__((always_inline)) {
-                      for (int q = 0; q < 4; ++q) v[q] *= alpha;
-                      store_sym<T>(A, d.mp, d.m, mirror, row0, col, v);
-                    });
+  const int64_t tr = (int64_t)ti * E::BM, tc = (int64_t)tj * E::BN;
+  const int m = d.m;
+  if constexpr (E::kStageTile) {
+    TileWalk<E>::apply(tr, tc, acc, [&](int64_t row0, int64_t col, float v[4]) __attribute__((always_inline)) {
+      for (int q = 0; q < 4; ++q) v[q] = (col < m && row0 + q < m) ? v[q] * alpha : 0.f;
+    });
+    store_tile_staged<E>(acc, static_cast<unsigned char*>(smem), A + tr * d.lda + tc, d.lda,
+                         mirror ? A + tc * d.lda + tr : nullptr, d.lda);
+  } else {
+    TileWalk<E>::each(tr, tc, acc, [&](int64_t row0, int64_t col, float v[4]) __attribute__((always_inline)) {
+      for (int q = 0; q < 4; ++q) v[q] *= alpha;
+      store_sym<T>(A, d.lda, m, mirror, row0, col, v);
+    });
+  }
 }
 
 template <class E>
@@ -421,39 +607,93 @@ MUON_INLINE void square_tile(const PhaseArgs& args, const MatDev& d, int ti, int
   typedef typename E::T T;
   const T* A = static_cast<const T*>(d.a);
   f32x16 acc[E::FM][E::FN];
-  E::run(A + (int64_t)ti * E::BM * d.mp, d.mp, A + (int64_t)tj * E::BN * d.mp, d.mp, d.mp,
+  E::run(A + (int64_t)ti * E::BM * d.lda, d.lda, A + (int64_t)tj * E::BN * d.lda, d.lda, d.mp,
          static_cast<T*>(smem), acc);
   T* B = static_cast<T*>(d.b);
   const float cb = args.co.b, cc = args.co.c;
   const bool mirror = ti != tj;
   const int64_t tr = (int64_t)ti * E::BM, tc = (int64_t)tj * E::BN;
-  if constexpr (E::kStageTile) stage_tile_bf16<E::NT>(A + tr * d.mp + tc, d.mp, static_cast<T*>(smem));
-  TileWalk<E>::each(tr, tc, acc,
-                    [&](int64_t row0, int64_t col, float v[4]) __attribute__((always_inline)) {
-                      // B = b*A + c*(A*A), formed in fp32 and rounded once.
-                      for (int q = 0; q < 4; ++q) {
-                        float aij;
-                        if constexpr (E::kStageTile)
-                          aij = lds_tile_bf16(static_cast<const u16*>(smem), row0 + q - tr, col - tc);
-                        else
-                          aij = Elem<T>::load(A + (row0 + q) * d.mp + col);
-                        v[q] = cb * aij + cc * v[q];
-                      }
-                      store_sym<T>(B, d.mp, d.m, mirror, row0, col, v);
-                    });
-  if constexpr (E::kStageTile) __syncthreads();
+  const int m = d.m;
+  if constexpr (E::kStageTile) {
+    // B = b*A + c*(A*A), formed in fp32 and rounded once.
+    stage_tile_bf16<E::NT>(A + tr * d.lda + tc, d.lda, static_cast<T*>(smem));
+    TileWalk<E>::apply(tr, tc, acc, [&](int64_t row0, int64_t col, float v[4]) __attribute__((always_inline)) {
+      for (int q = 0; q < 4; ++q) {
+        const float aij = lds_tile_bf16(static_cast<const u16*>(smem), row0 + q - tr, col - tc);
+        v[q] = (col < m && row0 + q < m) ? cb * aij + cc * v[q] : 0.f;
+      }
+    });
+    __syncthreads();  // every wave is done with the staged A tile
+    store_tile_staged<E>(acc, static_cast<unsigned char*>(smem), B + tr * d.lda + tc, d.lda,
+                         mirror ? B + tc * d.lda + tr : nullptr, d.lda);
+  } else {
+    TileWalk<E>::each(tr, tc, acc, [&](int64_t row0, int64_t col, float v[4]) __attribute__((always_inline)) {
+      for (int q = 0; q < 4; ++q) v[q] = cb * Elem<T>::load(A + (row0 + q) * d.lda + col) + cc * v[q];
+      store_sym<T>(B, d.lda, m, mirror, row0, col, v);
+    });
+  }
 }
 
-template <class E>
+// Last-iteration weight update through the staging tile: O (already in LDS
+// as bf16, in W's orientation) is applied to the W tile with origin
+// (wr0, wc0), 8 consecutive W elements per lane. W' = W - lr*scale*O and
+// delta = -lr*scale*O, each rounded once. Full, 16-byte aligned groups use
+// vector accesses; ragged or unaligned ones go element by element.
+template <int NT>
+MUON_INLINE void apply_from_lds(const unsigned char* smem, const MatDev& d, int64_t wr0, int64_t wc0) {
+  u16* W = static_cast<u16*>(d.w);
+  u16* D = static_cast<u16*>(d.delta);
+  const float ls = d.lr_scale;
+  const int64_t R = d.rows, C = d.cols;
+#pragma unroll 1
+  for (int p = 0; p < 256 * 32 / NT; ++p) {
+    const int idx = threadIdx.x + p * NT, row = idx >> 5, ch = idx & 31;
+    const int64_t gr = wr0 + row, gc = wc0 + ch * 8;
+    if (gr >= R || gc >= C) continue;
+    const u32x4 ov = *reinterpret_cast<const u32x4*>(smem + row * kOutStride + ch * 16);
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      o[2 * e] = __uint_as_float(ov[e] << 16);
+      o[2 * e + 1] = __uint_as_float(ov[e] & 0xffff0000u);
+    }
+    const int64_t base = gr * C + gc;
+    if (gc + 8 <= C && (base & 7) == 0) {
+      if (W) {
+        u32x4 wv = *((const g_u32x4*)(W + base));
+        u32x4 nv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          nv[e] = pack_bf16x2(__uint_as_float(wv[e] << 16) - ls * o[2 * e],
+                              __uint_as_float(wv[e] & 0xffff0000u) - ls * o[2 * e + 1]);
+        *((g_u32x4*)(W + base)) = nv;
+      }
+      if (D) {
+        u32x4 dv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dv[e] = pack_bf16x2(-ls * o[2 * e], -ls * o[2 * e + 1]);
+        *((g_u32x4*)(D + base)) = dv;
+      }
+    } else {
+      for (int e = 0; e < 8 && gc + e < C; ++e) {
+        if (W) Elem<u16>::store(W + base + e, Elem<u16>::load(W + base + e) - ls * o[e]);
+        if (D) Elem<u16>::store(D + base + e, -ls * o[e]);
+      }
+    }
+  }
+}
+
+template <class E, bool LAST>
 MUON_INLINE void update_tile(const PhaseArgs& args, const MatDev& d, int ti, int tj, void* smem) {
   typedef typename E::T T;
   const int src = args.src, dst = src ^ 1;
   const T* B = static_cast<const T*>(d.b);
   const T* Xt = static_cast<const T*>(d.xt[src]);
   f32x16 acc[E::FM][E::FN];
-  // (B X)[i][j] = sum_k B[i][k] X^T[j][k]
-  E::run(B + (int64_t)ti * E::BM * d.mp, d.mp, Xt + (int64_t)tj * E::BN * d.mp, d.mp, d.mp,
-         static_cast<T*>(smem), acc);
+  // (B X)[i][j] = sum_k B[i][k] X^T[j][k]. The bf16 engine also adds a*X[i][j]
+  // from the X^T panel while its K steps over this tile's rows are in LDS.
+  E::run(B + (int64_t)ti * E::BM * d.lda, d.lda, Xt + (int64_t)tj * E::BN * d.ldt, d.ldt, d.mp,
+         static_cast<T*>(smem), acc, E::kStageTile ? ti * (E::BM / E::BK) : -1, args.co.a);
   const T* X = static_cast<const T*>(d.x[src]);
   const float ca = args.co.a;
   // First iteration: X holds the unscaled U, and B was built from s*U, so
@@ -461,25 +701,37 @@ MUON_INLINE void update_tile(const PhaseArgs& args, const MatDev& d, int ti, int
   const float xs = args.first ? args.scale[&d - args.mats] : 1.f;
   const int m = d.m, n = d.n;
   const int64_t tr = (int64_t)ti * E::BM, tc = (int64_t)tj * E::BN;
-  if constexpr (E::kStageTile) stage_tile_bf16<E::NT>(X + tr * d.np + tc, d.np, static_cast<T*>(smem));
-  auto xval = [&](int64_t r, int64_t c) __attribute__((always_inline)) -> float {
-    if constexpr (E::kStageTile) return lds_tile_bf16(static_cast<const u16*>(smem), r - tr, c - tc);
-    else return Elem<T>::load(X + r * d.np + c);
-  };
-  if (!args.last) {
+  if constexpr (E::kStageTile) {
+    // acc already holds a*X + B*X.
+    TileWalk<E>::apply(tr, tc, acc, [&](int64_t row0, int64_t col, float v[4]) __attribute__((always_inline)) {
+      for (int q = 0; q < 4; ++q) v[q] = (col < n && row0 + q < m) ? xs * v[q] : 0.f;
+    });
+    unsigned char* sm = static_cast<unsigned char*>(smem);
+    if constexpr (!LAST) {
+      store_tile_staged<E>(acc, sm, static_cast<T*>(d.x[dst]) + tr * d.ldx + tc, d.ldx,
+                           static_cast<T*>(d.xt[dst]) + tc * d.ldt + tr, d.ldt);
+    } else {
+      // O = X_T, or X_T^T for a tall matrix: stage O in W's orientation.
+      acc_to_lds<E>(acc, sm, d.tall != 0);
+      __syncthreads();
+      apply_from_lds<E::NT>(sm, d, d.tall ? tc : tr, d.tall ? tr : tc);
+      __syncthreads();
+    }
+    return;
+  }
+  if constexpr (!LAST) {
     T* Xo = static_cast<T*>(d.x[dst]);
     T* Xto = static_cast<T*>(d.xt[dst]);
-    TileWalk<E>::each(tr, tc, acc,
-                      [&](int64_t row0, int64_t col, float v[4]) __attribute__((always_inline)) {
-                        const bool cok = col < n;
+    TileWalk<E>::each(tr, tc, acc, [&](int64_t row0, int64_t col, float v[4]) __attribute__((always_inline)) {
+      const bool cok = col < n;
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                          const int64_t o = (row0 + q) * d.np + col;
-                          v[q] = (cok && row0 + q < m) ? xs * (ca * xval(row0 + q, col) + v[q]) : 0.f;
-                          Elem<T>::store(Xo + o, v[q]);
-                        }
-                        Vec4<T>::store(Xto + col * d.mp + row0, v);
-                      });
+      for (int q = 0; q < 4; ++q) {
+        const int64_t o = (row0 + q) * d.ldx + col;
+        v[q] = (cok && row0 + q < m) ? xs * (ca * Elem<T>::load(X + o) + v[q]) : 0.f;
+        Elem<T>::store(Xo + o, v[q]);
+      }
+      Vec4<T>::store(Xto + col * d.ldt + row0, v);
+    });
   } else {
     // Last iteration: O = X_T (or X_T^T for a tall matrix).
     // W -= lr*scale*O, delta = -lr*scale*O.
@@ -487,28 +739,27 @@ MUON_INLINE void update_tile(const PhaseArgs& args, const MatDev& d, int ti, int
     T* D = static_cast<T*>(d.delta);
     const float ls = d.lr_scale;
     const int64_t ldw = d.cols;
-    TileWalk<E>::each(tr, tc, acc,
-                      [&](int64_t row0, int64_t col, float v[4]) __attribute__((always_inline)) {
-                        if (col >= n) return;
+    TileWalk<E>::each(tr, tc, acc, [&](int64_t row0, int64_t col, float v[4]) __attribute__((always_inline)) {
+      if (col >= n) return;
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                          const int64_t r = row0 + q;
-                          if (r >= m) break;
-                          const float o = xs * (ca * xval(r, col) + v[q]);
-                          const int64_t wo = d.tall ? col * ldw + r : r * ldw + col;
-                          if (W) Elem<T>::store(W + wo, Elem<T>::load(W + wo) - ls * o);
-                          if (D) Elem<T>::store(D + wo, -ls * o);
-                        }
-                      });
+      for (int q = 0; q < 4; ++q) {
+        const int64_t r = row0 + q;
+        if (r >= m) break;
+        const float o = xs * (ca * Elem<T>::load(X + r * d.ldx + col) + v[q]);
+        const int64_t wo = d.tall ? col * ldw + r : r * ldw + col;
+        if (W) Elem<T>::store(W + wo, Elem<T>::load(W + wo) - ls * o);
+        if (D) Elem<T>::store(D + wo, -ls * o);
+      }
+    });
   }
-  if constexpr (E::kStageTile) __syncthreads();
 }
 
 // ------------------------------------------------------------ persistent phase kernel
 
 template <class E, int PH>
 __global__ void __launch_bounds__(E::NT) phase_kernel(PhaseArgs args) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[E::LDS_BYTES];
+  constexpr int SMEM = E::kStageTile && kOutBytes > E::LDS_BYTES ? kOutBytes : E::LDS_BYTES;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
   __shared__ int s_tile;
   const int home = blockIdx.x % kQueues;
   for (int qq = 0; qq < kQueues; ++qq) {
@@ -525,7 +776,8 @@ __global__ void __launch_bounds__(E::NT) phase_kernel(PhaseArgs args) {
       const int ti = tile.ij >> 16, tj = tile.ij & 0xffff;
       if (PH == kGram) gram_tile<E>(args, d, ti, tj, smem);
       else if (PH == kSquare) square_tile<E>(args, d, ti, tj, smem);
-      else update_tile<E>(args, d, ti, tj, smem);
+      else if (PH == kUpdate) update_tile<E, false>(args, d, ti, tj, smem);
+      else update_tile<E, true>(args, d, ti, tj, smem);
     }
   }
 }
@@ -572,8 +824,8 @@ __global__ void __launch_bounds__(256) momentum_kernel(EwArgs args) {
   // U in its own orientation (rows x cols) and transposed (cols x rows).
   T* Ub = static_cast<T*>(d.tall ? d.xt[0] : d.x[0]);
   T* Utb = static_cast<T*>(d.tall ? d.x[0] : d.xt[0]);
-  const int64_t ldu = d.tall ? d.mp : d.np;
-  const int64_t ldut = d.tall ? d.np : d.mp;
+  const int64_t ldu = d.tall ? d.ldt : d.ldx;
+  const int64_t ldut = d.tall ? d.ldx : d.ldt;
   const float beta = args.co.beta;
   const bool nesterov = args.co.nesterov != 0;
   const bool vec_ok = (cols & 3) == 0;
@@ -663,7 +915,7 @@ __global__ void __launch_bounds__(256) apply_kernel(EwArgs args) {
   const int64_t r0 = (int64_t)(local / d.ew_tiles_c) * kEwTile;
   const int64_t c0 = (int64_t)(local % d.ew_tiles_c) * kEwTile;
   const T* Ub = static_cast<const T*>(d.tall ? d.xt[0] : d.x[0]);
-  const int64_t ldu = d.tall ? d.mp : d.np;
+  const int64_t ldu = d.tall ? d.ldt : d.ldx;
   T* W = static_cast<T*>(d.w);
   T* D = static_cast<T*>(d.delta);
   const float f = d.lr_scale * args.scale[mi];
@@ -702,7 +954,10 @@ static hipError_t launch_phase_e(Phase ph, const PhaseArgs& args, int32_t grid, 
   switch (ph) {
     case kGram: hipLaunchKernelGGL((phase_kernel<E, kGram>), dim3(grid), dim3(E::NT), 0, s, args); break;
     case kSquare: hipLaunchKernelGGL((phase_kernel<E, kSquare>), dim3(grid), dim3(E::NT), 0, s, args); break;
-    default: hipLaunchKernelGGL((phase_kernel<E, kUpdate>), dim3(grid), dim3(E::NT), 0, s, args); break;
+    default:
+      if (args.last) hipLaunchKernelGGL((phase_kernel<E, kUpdateLast>), dim3(grid), dim3(E::NT), 0, s, args);
+      else hipLaunchKernelGGL((phase_kernel<E, kUpdate>), dim3(grid), dim3(E::NT), 0, s, args);
+      break;
   }
   return hipGetLastError();
 }
