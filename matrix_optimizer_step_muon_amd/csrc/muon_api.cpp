@@ -175,7 +175,7 @@ muon_status muon_plan(const muon_matrix* mats, int32_t n, const muon_hparams* hp
 
   // Orientation, padding and workspace offsets.
   p->mats.resize(n);
-  std::vector<size_t> off(n * 6);
+  std::vector<size_t> off(n * 4);
   size_t cursor = 0;
   auto take = [&](size_t bytes) { size_t o = cursor; cursor = round_up(cursor + bytes, 256); return o; };
   std::vector<int32_t> prefix(n + 1, 0);
@@ -207,17 +207,13 @@ muon_status muon_plan(const muon_matrix* mats, int32_t n, const muon_hparams* hp
     // of a tile would fall on the same L2 channel.
     const int32_t skew = int32_t(128 / p->elem);
     d.ldx = d.np + skew;
-    d.ldt = d.mp + skew;
     d.lda = d.mp + skew;
     const size_t xbytes = size_t(d.mp) * d.ldx * p->elem;
-    const size_t tbytes = size_t(d.np) * d.ldt * p->elem;
     const size_t abytes = size_t(d.mp) * d.lda * p->elem;
-    off[i * 6 + 0] = take(xbytes);
-    off[i * 6 + 1] = take(xbytes);
-    off[i * 6 + 2] = take(tbytes);
-    off[i * 6 + 3] = take(tbytes);
-    off[i * 6 + 4] = take(abytes);
-    off[i * 6 + 5] = take(abytes);
+    off[i * 4 + 0] = take(xbytes);
+    off[i * 4 + 1] = take(xbytes);
+    off[i * 4 + 2] = take(abytes);
+    off[i * 4 + 3] = take(abytes);
   }
   p->ew_blocks = prefix[n];
   const size_t o_mats = take(sizeof(muon::MatDev) * n);
@@ -315,12 +311,10 @@ muon_status muon_plan(const muon_matrix* mats, int32_t n, const muon_hparams* hp
   if (e != hipSuccess) { free_plan(p); return hip_fail(e, "hipMemset"); }
   for (int32_t i = 0; i < n; ++i) {
     muon::MatDev& d = p->mats[i];
-    d.x[0] = base + off[i * 6 + 0];
-    d.x[1] = base + off[i * 6 + 1];
-    d.xt[0] = base + off[i * 6 + 2];
-    d.xt[1] = base + off[i * 6 + 3];
-    d.a = base + off[i * 6 + 4];
-    d.b = base + off[i * 6 + 5];
+    d.x[0] = base + off[i * 4 + 0];
+    d.x[1] = base + off[i * 4 + 1];
+    d.a = base + off[i * 4 + 2];
+    d.b = base + off[i * 4 + 3];
   }
   p->d_mats = reinterpret_cast<muon::MatDev*>(base + o_mats);
   p->d_prefix = reinterpret_cast<int32_t*>(base + o_prefix);

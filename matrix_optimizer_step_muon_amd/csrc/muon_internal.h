@@ -27,7 +27,6 @@ constexpr int kBlockCols = 8;
 // of U (m = min(rows, cols)): U itself, or U^T when rows > cols.
 struct MatDev {
   void* x[2];         // X ping/pong: mp x np, row-major, leading dimension ldx
-  void* xt[2];        // X^T ping/pong: np x mp, row-major, leading dimension ldt
   void* a;            // A = X X^T: mp x mp, leading dimension lda
   void* b;            // B = b*A + c*A*A: mp x mp, leading dimension lda
   void* w;            // weights rows x cols (may be null)
@@ -37,9 +36,9 @@ struct MatDev {
   int32_t rows, cols;
   int32_t m, n;       // m = min(rows, cols), n = max(rows, cols)
   int32_t mp, np;     // m, n rounded up to the GEMM tile edge
-  int32_t ldx, ldt, lda;  // row strides (elements) of X, X^T and A/B: the padded
-                          // width plus one 128-byte line, so the rows of a tile
-                          // spread over all L2 channels
+  int32_t ldx, lda;   // row strides (elements) of X and A/B: the padded width
+                      // plus one 128-byte line, so the rows of a tile spread
+                      // over all L2 channels
   int32_t tall;       // rows > cols
   int32_t ew_tiles_c; // elementwise tiles along cols: ceil(cols / 64)
   int32_t part_off;   // first norm-partial slot of this matrix

@@ -1,8 +1,8 @@
 // gfx950 (CDNA4) kernels of the whole-tensor Muon step.
 //
 // Kernels in one step, in launch order:
-//   momentum  fused M' = beta*M + G, U = G + beta*M' (Nesterov), U stored in
-//             both orientations, per-tile sums of squares (HBM-bound)
+//   momentum  fused M' = beta*M + G, U = G + beta*M' (Nesterov), U stored as
+//             X0 (transposed for a tall matrix), per-tile sums of squares (HBM-bound)
 //   norm      fixed-order reduction of those sums to s = 1/(||U||_F + eps)
 //   T times:
 //     gram    A = X X^T          symmetric: upper tiles only, each mirrored
@@ -21,11 +21,12 @@
 // first: the LPT rule the pages use to assign work to ranks (section 3.4,
 // "Why LPT ordering matters"), applied here across CUs.
 //
-// Both operands of every contraction are read along contiguous rows:
-// - X X^T: rows of X.
-// - A*A = A A^T: rows of A, since A is symmetric.
-// - B X: rows of B (symmetric) and rows of X^T, kept as a second copy.
-// So every GEMM is "NT", and each MFMA operand is a 16-byte LDS read.
+// Operands:
+// - X X^T and A*A = A A^T (A is symmetric) read both operands along
+//   contiguous rows: each MFMA operand is a 16-byte LDS read.
+// - B X reads rows of B (symmetric) and X with K as its row index, through the
+//   transposing LDS load ds_read_b64_tr_b16. So X is kept in one orientation
+//   only.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -153,7 +154,29 @@ MUON_INLINE int lds_swizzle(int r) {
   return (r & 7) ^ ((r >> 3) & 1);
 }
 
-template <int WAVES_M, int WAVES_N, int BK_, int STAGES_>
+// Q operand stored K-major (QK engines): LDS rows are K indices of 256 bf16
+// (512 bytes, 32 slots). The slot of chunk c of row k is c ^ swzk(k), which
+// keeps the transposing fragment reads below free of bank conflicts for 32-
+// and 64-bank LDS. It depends only on k % 4.
+MUON_INLINE int lds_swizzle_k(int k) { return ((k & 1) ? 4 : 0) ^ ((k & 2) ? 10 : 0); }
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
+// i % 4 of the 4 x 16-bit values at the address of lane 4e + i/4, for
+// e = 0..3. If lane j of the group points at row k0 + j/4, columns
+// n0 + 4(j%4) .. +3 of a K-major tile, lane i gets column n0 + i at rows
+// k0 .. k0+3: the B-operand fragment layout of the MFMA.
+MUON_INLINE v4i16 lds_read_tr(const unsigned char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)(const_cast<unsigned char*>(p)));
+}
+
+// QK = false: both operands are row-major with K contiguous (C = P Q^T).
+// QK = true: Q is row-major with K as its row index (C = P Q), read through
+// transposing LDS loads, so no transposed copy of Q is needed.
+template <int WAVES_M, int WAVES_N, int BK_, int STAGES_, bool QK>
 struct EngineBF16 {
   typedef u16 T;
   static constexpr int BM = 256, BN = 256, BK = BK_;
@@ -162,22 +185,23 @@ struct EngineBF16 {
   static constexpr int NW = NT / 64;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   static constexpr int FM = WM / 32, FN = WN / 32;
-  static constexpr int S = BK / 8;                  // 16-byte slots per LDS row
-  static constexpr int ROW = BK * 2;                // LDS row bytes
-  static constexpr int RPI = 1024 / ROW;            // rows per DMA wave instruction
-  static constexpr int OP_BYTES = BM * ROW;         // one operand tile of one stage
-  static constexpr int STAGE_BYTES = 2 * OP_BYTES;  // P and Q
+  static constexpr int S = BK / 8;                  // 16-byte slots per P row
+  static constexpr int ROW = BK * 2;                // P row bytes
+  static constexpr int RPI = 1024 / ROW;            // P rows per DMA wave instruction
+  static constexpr int OP_BYTES = BM * ROW;         // one operand tile of one stage (P or Q)
+  static constexpr int STAGE_BYTES = 2 * OP_BYTES;
   static constexpr int DPW = OP_BYTES / 1024 / NW;  // DMA instructions per wave per operand
   static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
   static constexpr bool kStageTile = true;          // epilogue operand tiles go through LDS
+  static constexpr bool kQK = QK;
   static MUON_INLINE int wave_m(int w) { return w / WAVES_N; }
   static MUON_INLINE int wave_n(int w) { return w % WAVES_N; }
 
-  // diag_kt0 >= 0 (update phase only): the Q operand is the X^T panel of the
-  // output tile's columns, and its K steps diag_kt0 .. diag_kt0 + BM/BK - 1
-  // hold X^T over the tile's own rows. While those steps are in LDS, the waves
-  // that own the matching output rows add diag_coef * X[r][c] to their
-  // accumulators, so the a*X term of X' = a*X + B*X needs no separate read of X.
+  // diag_kt0 >= 0 (QK only; the update phase): Q is the X panel of the output
+  // tile's columns, and its K steps diag_kt0 .. diag_kt0 + BM/BK - 1 hold X
+  // over the tile's own rows. While those steps are in LDS, the waves that own
+  // the matching output rows add diag_coef * X[r][c] to their accumulators, so
+  // the a*X term of X' = a*X + B*X needs no separate read of X.
   static MUON_INLINE void run(const u16* __restrict__ P, int64_t ldp, const u16* __restrict__ Q,
                               int64_t ldq, int K, u16* smem, f32x16 (&acc)[FM][FN],
                               int diag_kt0 = -1, float diag_coef = 0.f) {
@@ -190,9 +214,11 @@ struct EngineBF16 {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    // DMA plan: instruction (wave, p) of an operand fills rows
-    // RPI*(wave*DPW + p) .. +RPI of the stage. Lane l carries row + l/S, slot
-    // l%S, i.e. the global chunk slot ^ swz(row).
+    // DMA plan. P (and Q unless QK): instruction (wave, p) fills rows
+    // RPI*(wave*DPW + p) .. +RPI of the stage; lane l carries row + l/S, slot
+    // l%S, i.e. the global chunk slot ^ swz(row). QK: instruction (wave, p)
+    // fills K rows 2*(wave*DPW + p) .. +1 of 512 bytes; lane l carries row
+    // + l/32, slot l%32, i.e. the global chunk slot ^ swzk(row).
     const uint32_t lds_base = (uint32_t)(uintptr_t)smem;
     const u16* gp[DPW];
     const u16* gq[DPW];
@@ -201,22 +227,40 @@ struct EngineBF16 {
       const int row = (wave * DPW + p) * RPI + lane / S;
       const int ch = (lane % S) ^ lds_swizzle<S>(row);
       gp[p] = P + row * ldp + ch * 8;
-      gq[p] = Q + row * ldq + ch * 8;
+      if (QK) {
+        const int kr = (wave * DPW + p) * 2 + (lane >> 5);
+        gq[p] = Q + kr * ldq + ((lane & 31) ^ lds_swizzle_k(kr)) * 8;
+      } else {
+        gq[p] = Q + row * ldq + ch * 8;
+      }
     }
+    const int64_t qstep = QK ? (int64_t)BK * ldq : BK;  // Q elements per K step
     auto issue = [&](int kt) __attribute__((always_inline)) {
       const uint32_t st = lds_base + (kt % STAGES) * STAGE_BYTES;
 #pragma unroll
       for (int p = 0; p < DPW; ++p) {
         const uint32_t off = (wave * DPW + p) * 1024;
         dma16(gp[p] + kt * BK, __builtin_amdgcn_readfirstlane(st + off));
-        dma16(gq[p] + kt * BK, __builtin_amdgcn_readfirstlane(st + OP_BYTES + off));
+        dma16(gq[p] + kt * qstep, __builtin_amdgcn_readfirstlane(st + OP_BYTES + off));
       }
     };
-    // Fragment reads: lane l reads row l % 32 of each 32-row block, 16-byte
+    // P fragment reads: lane l reads row l % 32 of each 32-row block, 16-byte
     // chunk 2*kk + l/32, at slot chunk ^ swz(row).
     const int r32 = lane & 31, h = lane >> 5, sw = lds_swizzle<S>(r32);
     const unsigned char* sb = reinterpret_cast<const unsigned char*>(smem);
     const uint32_t rowp = (wm * WM + r32) * ROW, rowq = OP_BYTES + (wn * WN + r32) * ROW;
+    // QK fragment reads: in lane group G = l/16, lane i16 = l%16 points at K
+    // row 8*(G/2) + i16/4 (+16 kk, +4 for the upper half) and columns
+    // wn*WN + 32j + 16*(G%2) + 4*(i16%4) .. +3.
+    const int G = lane >> 4, i16 = lane & 15;
+    const uint32_t qrow = OP_BYTES + (8 * (G >> 1) + (i16 >> 2)) * 512;
+    const uint32_t drow = OP_BYTES + (4 * (G >> 1) + (i16 >> 2)) * 512;  // diag reads: 4-row groups
+    uint32_t qcol[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int chunk = (wn * WN + 32 * j + 16 * (G & 1) + 4 * (i16 & 3)) >> 3;
+      qcol[j] = ((chunk ^ lds_swizzle_k(i16 >> 2)) << 4) + 8 * (i16 & 1);
+    }
 
     // Register fragments are double-buffered: the reads of sub-step kk+1 are
     // in flight while the MFMAs of sub-step kk run.
@@ -228,7 +272,15 @@ struct EngineBF16 {
 #pragma unroll
       for (int i = 0; i < FM; ++i) fp[buf][i] = *reinterpret_cast<const bf16x8*>(st + rowp + i * 32 * ROW + fo);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) fq[buf][j] = *reinterpret_cast<const bf16x8*>(st + rowq + j * 32 * ROW + fo);
+      for (int j = 0; j < FN; ++j) {
+        if (QK) {
+          const unsigned char* q = st + qrow + kk * 16 * 512 + qcol[j];
+          const v4i16 lo = lds_read_tr(q), hi = lds_read_tr(q + 4 * 512);
+          fq[buf][j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        } else {
+          fq[buf][j] = *reinterpret_cast<const bf16x8*>(st + rowq + j * 32 * ROW + fo);
+        }
+      }
     };
     auto mfmas = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
@@ -240,32 +292,25 @@ struct EngineBF16 {
     // K step kt of the diagonal window covers tile rows slab*BK .. +BK, with
     // slab = kt - diag_kt0. Accumulator group (i, j, g) of this lane holds
     // rows R .. R+3, R = wm*WM + 32i + 8g + 4(l/32), of column
-    // c = wn*WN + 32j + l%32. X[R + q][c] sits in Q-stage row c at k offset
-    // R + q - slab*BK: 4 consecutive bf16, one 8-byte LDS read.
+    // c = wn*WN + 32j + l%32: one transposing read at K rows R - slab*BK.
     auto diag_add = [&](int kt) __attribute__((always_inline)) {
+      if (!QK) return;
       const int slab = kt - diag_kt0;
       if (diag_kt0 < 0 || slab < 0 || slab >= BM / BK) return;
-      const unsigned char* st = sb + (kt % STAGES) * STAGE_BYTES + OP_BYTES;
+      const unsigned char* st = sb + (kt % STAGES) * STAGE_BYTES + drow;
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        const int rbase = wm * WM + i * 32 + 4 * h - slab * BK;  // k offset of row R for g = 0
-        if (rbase + 28 < 0 || rbase >= BK) continue;              // block outside this slab
+        const int r0 = wm * WM + i * 32 - slab * BK;  // K row of the block's first row
+        if (r0 < 0 || r0 + 32 > BK) continue;         // block outside this slab
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int c = wn * WN + j * 32 + r32;
-          const unsigned char* rowc = st + c * ROW;
-          const int swc = lds_swizzle<S>(c);
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const int ko = rbase + 8 * g;
-            if (ko < 0 || ko >= BK) continue;
-            const u32x2 v = *reinterpret_cast<const u32x2*>(rowc + (((ko >> 3) ^ swc) << 4) + (ko & 7) * 2);
-            acc[i][j][4 * g + 0] += diag_coef * __uint_as_float(v[0] << 16);
-            acc[i][j][4 * g + 1] += diag_coef * __uint_as_float(v[0] & 0xffff0000u);
-            acc[i][j][4 * g + 2] += diag_coef * __uint_as_float(v[1] << 16);
-            acc[i][j][4 * g + 3] += diag_coef * __uint_as_float(v[1] & 0xffff0000u);
+            const v4i16 v = lds_read_tr(st + (r0 + 8 * g) * 512 + qcol[j]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              acc[i][j][4 * g + e] += diag_coef * __uint_as_float((uint32_t)(uint16_t)v[e] << 16);
           }
-        }
       }
     };
     const int KT = K / BK;
@@ -319,17 +364,22 @@ struct EngineBF16 {
   }
 };
 
+template <bool QK>
 struct EngineF32 {
   typedef float T;
   static constexpr int BM = 128, BN = 128, BK = 32, NT = 256;
   static constexpr int WM = 64, WN = 64;     // wave tile: 4 waves as 2 x 2
   static constexpr int FM = WM / 32, FN = WN / 32;
   static constexpr int LDS_STRIDE = BK + 1;  // floats; odd stride spreads rows over banks
-  static constexpr int STAGE = (BM + BN) * LDS_STRIDE;
+  static constexpr int QK_STRIDE = BN + 4;   // floats per K row of a K-major Q tile
+  static constexpr int PART = BM * LDS_STRIDE;  // = BK * QK_STRIDE: P and Q parts are the same size
+  static constexpr int STAGE = 2 * PART;
   static constexpr int LDS_BYTES = 2 * STAGE * 4;
   static constexpr bool kStageTile = false;
+  static constexpr bool kQK = QK;
   static MUON_INLINE int wave_m(int w) { return w >> 1; }
   static MUON_INLINE int wave_n(int w) { return w & 1; }
+  static_assert(BM * LDS_STRIDE == BK * QK_STRIDE, "P and Q parts of a stage differ in size");
 
   static MUON_INLINE void run(const float* __restrict__ P, int64_t ldp, const float* __restrict__ Q,
                               int64_t ldq, int K, float* smem, f32x16 (&acc)[FM][FN], int = -1, float = 0.f) {
@@ -342,23 +392,26 @@ struct EngineF32 {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+    // P: 128 rows x 32 floats (8 chunks per row). Q, QK: 32 K rows x 128
+    // floats (32 chunks per row); otherwise like P.
     u32x4 rp[4], rq[4];
     auto gload = [&](int k0) __attribute__((always_inline)) {
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        const int q = tid + p * NT, row = q >> 3, ch = q & 7;
-        rp[p] = gload16(P + row * ldp + k0 + ch * 4);
-        rq[p] = gload16(Q + row * ldq + k0 + ch * 4);
+        const int q = tid + p * NT;
+        rp[p] = gload16(P + (q >> 3) * ldp + k0 + (q & 7) * 4);
+        if (QK) rq[p] = gload16(Q + (int64_t)(k0 + (q >> 5)) * ldq + (q & 31) * 4);
+        else rq[p] = gload16(Q + (q >> 3) * ldq + k0 + (q & 7) * 4);
       }
     };
     auto sstore = [&](int s) __attribute__((always_inline)) {
       float* sp = smem + s * STAGE;
-      float* sq = sp + BM * LDS_STRIDE;
+      float* sq = sp + PART;
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        const int q = tid + p * NT, row = q >> 3, ch = q & 7;
-        float* dp = sp + row * LDS_STRIDE + ch * 4;
-        float* dq = sq + row * LDS_STRIDE + ch * 4;
+        const int q = tid + p * NT;
+        float* dp = sp + (q >> 3) * LDS_STRIDE + (q & 7) * 4;
+        float* dq = QK ? sq + (q >> 5) * QK_STRIDE + (q & 31) * 4 : sq + (q >> 3) * LDS_STRIDE + (q & 7) * 4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           dp[e] = __uint_as_float(rp[p][e]);
@@ -375,15 +428,15 @@ struct EngineF32 {
       const int s = kt & 1;
       if (kt + 1 < KT) gload((kt + 1) * BK);
       const float* sp = smem + s * STAGE + (wm * WM + (lane & 31)) * LDS_STRIDE + (lane >> 5);
-      const float* sq = smem + s * STAGE + BM * LDS_STRIDE + (wn * WN + (lane & 31)) * LDS_STRIDE +
-                        (lane >> 5);
+      const float* sq = QK ? smem + s * STAGE + PART + (lane >> 5) * QK_STRIDE + wn * WN + (lane & 31)
+                           : smem + s * STAGE + PART + (wn * WN + (lane & 31)) * LDS_STRIDE + (lane >> 5);
 #pragma unroll
       for (int kk = 0; kk < BK / 2; ++kk) {
         float fp[FM], fq[FN];
 #pragma unroll
         for (int i = 0; i < FM; ++i) fp[i] = sp[i * 32 * LDS_STRIDE + kk * 2];
 #pragma unroll
-        for (int j = 0; j < FN; ++j) fq[j] = sq[j * 32 * LDS_STRIDE + kk * 2];
+        for (int j = 0; j < FN; ++j) fq[j] = QK ? sq[kk * 2 * QK_STRIDE + j * 32] : sq[j * 32 * LDS_STRIDE + kk * 2];
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -685,22 +738,22 @@ MUON_INLINE void apply_from_lds(const unsigned char* smem, const MatDev& d, int6
 
 template <class E, bool LAST>
 MUON_INLINE void update_tile(const PhaseArgs& args, const MatDev& d, int ti, int tj, void* smem) {
+  static_assert(E::kQK, "the update reads X as a K-major operand");
   typedef typename E::T T;
   const int src = args.src, dst = src ^ 1;
   const T* B = static_cast<const T*>(d.b);
-  const T* Xt = static_cast<const T*>(d.xt[src]);
-  f32x16 acc[E::FM][E::FN];
-  // (B X)[i][j] = sum_k B[i][k] X^T[j][k]. The bf16 engine also adds a*X[i][j]
-  // from the X^T panel while its K steps over this tile's rows are in LDS.
-  E::run(B + (int64_t)ti * E::BM * d.lda, d.lda, Xt + (int64_t)tj * E::BN * d.ldt, d.ldt, d.mp,
-         static_cast<T*>(smem), acc, E::kStageTile ? ti * (E::BM / E::BK) : -1, args.co.a);
   const T* X = static_cast<const T*>(d.x[src]);
+  const int64_t tr = (int64_t)ti * E::BM, tc = (int64_t)tj * E::BN;
+  f32x16 acc[E::FM][E::FN];
+  // (B X)[i][j] = sum_k B[i][k] X[k][j]. The bf16 engine also adds a*X[i][j]
+  // while its K steps over this tile's rows are in LDS.
+  E::run(B + tr * d.lda, d.lda, X + tc, d.ldx, d.mp, static_cast<T*>(smem), acc,
+         E::kStageTile ? ti * (E::BM / E::BK) : -1, args.co.a);
   const float ca = args.co.a;
   // First iteration: X holds the unscaled U, and B was built from s*U, so
   // X1 = s * (a U + B U).
   const float xs = args.first ? args.scale[&d - args.mats] : 1.f;
   const int m = d.m, n = d.n;
-  const int64_t tr = (int64_t)ti * E::BM, tc = (int64_t)tj * E::BN;
   if constexpr (E::kStageTile) {
     // acc already holds a*X + B*X.
     TileWalk<E>::apply(tr, tc, acc, [&](int64_t row0, int64_t col, float v[4]) __attribute__((always_inline)) {
@@ -708,8 +761,7 @@ MUON_INLINE void update_tile(const PhaseArgs& args, const MatDev& d, int ti, int
     });
     unsigned char* sm = static_cast<unsigned char*>(smem);
     if constexpr (!LAST) {
-      store_tile_staged<E>(acc, sm, static_cast<T*>(d.x[dst]) + tr * d.ldx + tc, d.ldx,
-                           static_cast<T*>(d.xt[dst]) + tc * d.ldt + tr, d.ldt);
+      store_tile_staged<E>(acc, sm, static_cast<T*>(d.x[dst]) + tr * d.ldx + tc, d.ldx, nullptr, 0);
     } else {
       // O = X_T, or X_T^T for a tall matrix: stage O in W's orientation.
       acc_to_lds<E>(acc, sm, d.tall != 0);
@@ -721,16 +773,13 @@ MUON_INLINE void update_tile(const PhaseArgs& args, const MatDev& d, int ti, int
   }
   if constexpr (!LAST) {
     T* Xo = static_cast<T*>(d.x[dst]);
-    T* Xto = static_cast<T*>(d.xt[dst]);
     TileWalk<E>::each(tr, tc, acc, [&](int64_t row0, int64_t col, float v[4]) __attribute__((always_inline)) {
       const bool cok = col < n;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int64_t o = (row0 + q) * d.ldx + col;
-        v[q] = (cok && row0 + q < m) ? xs * (ca * Elem<T>::load(X + o) + v[q]) : 0.f;
-        Elem<T>::store(Xo + o, v[q]);
+        Elem<T>::store(Xo + o, (cok && row0 + q < m) ? xs * (ca * Elem<T>::load(X + o) + v[q]) : 0.f);
       }
-      Vec4<T>::store(Xto + col * d.ldt + row0, v);
     });
   } else {
     // Last iteration: O = X_T (or X_T^T for a tall matrix).
@@ -774,9 +823,9 @@ __global__ void __launch_bounds__(E::NT) phase_kernel(PhaseArgs args) {
       const Tile tile = args.tiles[base + t];
       const MatDev& d = args.mats[tile.mat];
       const int ti = tile.ij >> 16, tj = tile.ij & 0xffff;
-      if (PH == kGram) gram_tile<E>(args, d, ti, tj, smem);
-      else if (PH == kSquare) square_tile<E>(args, d, ti, tj, smem);
-      else if (PH == kUpdate) update_tile<E, false>(args, d, ti, tj, smem);
+      if constexpr (PH == kGram) gram_tile<E>(args, d, ti, tj, smem);
+      else if constexpr (PH == kSquare) square_tile<E>(args, d, ti, tj, smem);
+      else if constexpr (PH == kUpdate) update_tile<E, false>(args, d, ti, tj, smem);
       else update_tile<E, true>(args, d, ti, tj, smem);
     }
   }
@@ -821,11 +870,11 @@ __global__ void __launch_bounds__(256) momentum_kernel(EwArgs args) {
   const int rows = d.rows, cols = d.cols;
   const T* G = static_cast<const T*>(d.g);
   T* Mo = static_cast<T*>(d.mom);
-  // U in its own orientation (rows x cols) and transposed (cols x rows).
-  T* Ub = static_cast<T*>(d.tall ? d.xt[0] : d.x[0]);
-  T* Utb = static_cast<T*>(d.tall ? d.x[0] : d.xt[0]);
-  const int64_t ldu = d.tall ? d.ldt : d.ldx;
-  const int64_t ldut = d.tall ? d.ldx : d.ldt;
+  // X0 = U (rows <= cols) or U^T (tall), in the X buffer: a wide matrix is
+  // stored directly, a tall one through the LDS tile, transposed.
+  T* Xb = static_cast<T*>(d.x[0]);
+  const int64_t ldx = d.ldx;
+  const bool tall = d.tall != 0;
   const float beta = args.co.beta;
   const bool nesterov = args.co.nesterov != 0;
   const bool vec_ok = (cols & 3) == 0;
@@ -848,7 +897,7 @@ __global__ void __launch_bounds__(256) momentum_kernel(EwArgs args) {
           u[e] = nesterov ? g[e] + beta * mn[e] : mn[e];
         }
         Vec4<T>::store(Mo + o, mn);
-        Vec4<T>::store(Ub + gr * ldu + gc, u);
+        if (!tall) Vec4<T>::store(Xb + gr * ldx + gc, u);
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -857,7 +906,7 @@ __global__ void __launch_bounds__(256) momentum_kernel(EwArgs args) {
             const float mn = beta * Elem<T>::load(Mo + o + e) + g;
             u[e] = nesterov ? g + beta * mn : mn;
             Elem<T>::store(Mo + o + e, mn);
-            Elem<T>::store(Ub + gr * ldu + gc + e, u[e]);
+            if (!tall) Elem<T>::store(Xb + gr * ldx + gc + e, u[e]);
           }
         }
       }
@@ -871,13 +920,14 @@ __global__ void __launch_bounds__(256) momentum_kernel(EwArgs args) {
   const float tot = block_sum_256(ss, red);  // contains a barrier: tileU is complete
   if (tid == 0) args.partials[d.part_off + local] = tot;
 
-  // Transposed copy: row gc of U^T holds column gc of U.
+  if (!tall) return;
+  // Tall matrix: row gc of X = U^T holds column gc of U.
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const int lc = p * 16 + (tid >> 4), lr = (tid & 15) * 4;
     const int64_t gc = c0 + lc, gr = r0 + lr;
     if (gc >= cols) continue;
-    T* dst = Utb + gc * ldut + gr;
+    T* dst = Xb + gc * ldx + gr;
     if (gr + 3 < rows) {
       float v[4];
 #pragma unroll
@@ -914,15 +964,14 @@ __global__ void __launch_bounds__(256) apply_kernel(EwArgs args) {
   const int local = blockIdx.x - args.prefix[mi];
   const int64_t r0 = (int64_t)(local / d.ew_tiles_c) * kEwTile;
   const int64_t c0 = (int64_t)(local % d.ew_tiles_c) * kEwTile;
-  const T* Ub = static_cast<const T*>(d.tall ? d.xt[0] : d.x[0]);
-  const int64_t ldu = d.tall ? d.ldt : d.ldx;
+  const T* Xb = static_cast<const T*>(d.x[0]);  // U, or U^T for a tall matrix
   T* W = static_cast<T*>(d.w);
   T* D = static_cast<T*>(d.delta);
   const float f = d.lr_scale * args.scale[mi];
   for (int e = threadIdx.x; e < kEwTile * kEwTile; e += 256) {
     const int64_t gr = r0 + e / kEwTile, gc = c0 + e % kEwTile;
     if (gr >= d.rows || gc >= d.cols) continue;
-    const float o = f * Elem<T>::load(Ub + gr * ldu + gc);
+    const float o = f * Elem<T>::load(Xb + (d.tall ? gc * d.ldx + gr : gr * d.ldx + gc));
     const int64_t wo = gr * d.cols + gc;
     if (W) Elem<T>::store(W + wo, Elem<T>::load(W + wo) - o);
     if (D) Elem<T>::store(D + wo, -o);
@@ -949,14 +998,16 @@ hipError_t launch_apply(int dtype, const EwArgs& args, int32_t n_blocks, hipStre
   return hipGetLastError();
 }
 
-template <class E>
+// E reads both operands along K (gram, square); EQ reads Q as a K-major
+// operand (update).
+template <class E, class EQ>
 static hipError_t launch_phase_e(Phase ph, const PhaseArgs& args, int32_t grid, hipStream_t s) {
   switch (ph) {
     case kGram: hipLaunchKernelGGL((phase_kernel<E, kGram>), dim3(grid), dim3(E::NT), 0, s, args); break;
     case kSquare: hipLaunchKernelGGL((phase_kernel<E, kSquare>), dim3(grid), dim3(E::NT), 0, s, args); break;
     default:
-      if (args.last) hipLaunchKernelGGL((phase_kernel<E, kUpdateLast>), dim3(grid), dim3(E::NT), 0, s, args);
-      else hipLaunchKernelGGL((phase_kernel<E, kUpdate>), dim3(grid), dim3(E::NT), 0, s, args);
+      if (args.last) hipLaunchKernelGGL((phase_kernel<EQ, kUpdateLast>), dim3(grid), dim3(EQ::NT), 0, s, args);
+      else hipLaunchKernelGGL((phase_kernel<EQ, kUpdate>), dim3(grid), dim3(EQ::NT), 0, s, args);
       break;
   }
   return hipGetLastError();
@@ -964,9 +1015,10 @@ static hipError_t launch_phase_e(Phase ph, const PhaseArgs& args, int32_t grid, 
 
 hipError_t launch_phase(int dtype, int variant, Phase ph, const PhaseArgs& args, int32_t grid,
                         hipStream_t s) {
-  if (dtype != 1) return launch_phase_e<EngineF32>(ph, args, grid, s);
-  if (variant == kGemmBK32) return launch_phase_e<EngineBF16<2, 4, 32, 4>>(ph, args, grid, s);
-  return launch_phase_e<EngineBF16<2, 4, 64, 2>>(ph, args, grid, s);
+  if (dtype != 1) return launch_phase_e<EngineF32<false>, EngineF32<true>>(ph, args, grid, s);
+  if (variant == kGemmBK32)
+    return launch_phase_e<EngineBF16<2, 4, 32, 4, false>, EngineBF16<2, 4, 32, 4, true>>(ph, args, grid, s);
+  return launch_phase_e<EngineBF16<2, 4, 64, 2, false>, EngineBF16<2, 4, 64, 2, true>>(ph, args, grid, s);
 }
 
 int gemm_blocks_per_cu(int dtype, int variant) {
