@@ -60,12 +60,13 @@ MUON_INLINE u32x4 gload16(const void* p) { return *((const g_u32x4*)(p)); }
 
 MUON_INLINE float bf16_to_f32(u16 v) { return __uint_as_float((uint32_t)v << 16); }
 
-// Round to nearest even; NaN stays a (quiet) NaN.
-MUON_INLINE u16 f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u16)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (u16)(u >> 16);
+// fp32 -> bf16 with gfx950's v_cvt_pk_bf16_f32: rounds to nearest even under
+// the default rounding mode, and a NaN stays a quiet NaN.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+MUON_INLINE u16 f32_to_bf16(float f) { return __builtin_bit_cast(u16, (__bf16)f); }
+MUON_INLINE uint32_t pack_bf16x2(float lo, float hi) {
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 template <class T> struct Elem;
@@ -104,8 +105,8 @@ template <> struct Vec4<u16> {
   }
   static MUON_INLINE void store(u16* p, const float v[4]) {
     u32x2 t;
-    t[0] = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-    t[1] = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+    t[0] = pack_bf16x2(v[0], v[1]);
+    t[1] = pack_bf16x2(v[2], v[3]);
     *((g_u32x2*)(p)) = t;
   }
 };
@@ -114,10 +115,13 @@ template <> struct Vec4<u16> {
 //
 // Each engine computes one BM x BN output tile, C[i][j] = sum_k P[i][k] Q[j][k]
 // (P, Q row-major, K a multiple of BK), and leaves it in MFMA accumulators.
-// Accumulator layout of a 32 x 32 MFMA block, element r of lane l:
-//   column = l % 32,  row = 8*(r/4) + 4*(l/32) + r%4.
-// The engines differ in their wave layout. WAVES_M x WAVES_N waves each own a
-// WM x WN sub-tile; fewer, larger wave tiles read less LDS per flop.
+// A 32 x 32 MFMA block D = A B^T puts A's rows in its registers and B's rows
+// on its lanes: element r of lane l is D[8*(r/4) + 4*(l/32) + r%4][l % 32].
+// The fp32 engine passes (P, Q): lane l holds output column l % 32 and four
+// runs of 4 consecutive rows. The bf16 engine passes (Q, P): lane l holds
+// output row l % 32 and four runs of 4 consecutive columns, which its
+// epilogue writes as 8-byte units. WAVES_M x WAVES_N waves each own a WM x WN
+// sub-tile; fewer, larger wave tiles read less LDS per flop.
 
 // Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4).
 // Lane l's bytes land at LDS address lds + 16*l, so one wave instruction
@@ -197,11 +201,12 @@ struct EngineBF16 {
   static MUON_INLINE int wave_m(int w) { return w / WAVES_N; }
   static MUON_INLINE int wave_n(int w) { return w % WAVES_N; }
 
-  // diag_kt0 >= 0 (QK only; the update phase): Q is the X panel of the output
-  // tile's columns, and its K steps diag_kt0 .. diag_kt0 + BM/BK - 1 hold X
-  // over the tile's own rows. While those steps are in LDS, the waves that own
-  // the matching output rows add diag_coef * X[r][c] to their accumulators, so
-  // the a*X term of X' = a*X + B*X needs no separate read of X.
+  // diag_kt0 >= 0 adds diag_coef times a tile of the operands to the
+  // product, read while it is in LDS anyway. Update (QK): Q is the X panel of
+  // the output tile's columns, and its K steps diag_kt0 .. +BM/BK-1 hold X over
+  // the tile's own rows, so the a*X term of X' = a*X + B*X needs no separate
+  // read of X. Square: P is the A panel of the tile's rows, and its K steps
+  // diag_kt0 .. +BN/BK-1 hold A over the tile's own columns, for the b*A term.
   static MUON_INLINE void run(const u16* __restrict__ P, int64_t ldp, const u16* __restrict__ Q,
                               int64_t ldq, int K, u16* smem, f32x16 (&acc)[FM][FN],
                               int diag_kt0 = -1, float diag_coef = 0.f) {
@@ -254,7 +259,6 @@ struct EngineBF16 {
     // wn*WN + 32j + 16*(G%2) + 4*(i16%4) .. +3.
     const int G = lane >> 4, i16 = lane & 15;
     const uint32_t qrow = OP_BYTES + (8 * (G >> 1) + (i16 >> 2)) * 512;
-    const uint32_t drow = OP_BYTES + (4 * (G >> 1) + (i16 >> 2)) * 512;  // diag reads: 4-row groups
     uint32_t qcol[FN];
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
@@ -287,31 +291,52 @@ struct EngineBF16 {
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp[buf][i], fq[buf][j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fq[buf][j], fp[buf][i], acc[i][j], 0, 0, 0);
     };
-    // K step kt of the diagonal window covers tile rows slab*BK .. +BK, with
-    // slab = kt - diag_kt0. Accumulator group (i, j, g) of this lane holds
-    // rows R .. R+3, R = wm*WM + 32i + 8g + 4(l/32), of column
-    // c = wn*WN + 32j + l%32: one transposing read at K rows R - slab*BK.
+    // Diagonal window: K steps diag_kt0 .. diag_kt0 + BM/BK - 1 (slab =
+    // kt - diag_kt0) hold the output tile's own rows (QK: Q's K rows) or
+    // columns (otherwise: P's K columns) slab*BK .. +BK. Accumulator group
+    // (i, j, g) of lane l holds row R = wm*WM + 32i + l%32, columns
+    // C .. C+3 with C = wn*WN + 32j + 8g + 4(l/32): one 8-byte read of the
+    // operand row R - slab*BK (QK) or of P row R at K column C - slab*BK.
     auto diag_add = [&](int kt) __attribute__((always_inline)) {
-      if (!QK) return;
       const int slab = kt - diag_kt0;
       if (diag_kt0 < 0 || slab < 0 || slab >= BM / BK) return;
-      const unsigned char* st = sb + (kt % STAGES) * STAGE_BYTES + drow;
+      const unsigned char* st = sb + (kt % STAGES) * STAGE_BYTES;
+      const int h8 = 8 * h;
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int r0 = wm * WM + i * 32 - slab * BK;  // K row of the block's first row
-        if (r0 < 0 || r0 + 32 > BK) continue;         // block outside this slab
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
+        for (int j = 0; j < FN; ++j) {
+          if (QK) {
+            const int k0 = wm * WM + i * 32 - slab * BK;  // K row of the block's first row
+            if (k0 < 0 || k0 + 32 > BK) continue;         // block outside this slab
+            const int kr = k0 + r32;
+            const unsigned char* row = st + OP_BYTES + kr * 512 + h8;
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const v4i16 v = lds_read_tr(st + (r0 + 8 * g) * 512 + qcol[j]);
+            for (int g = 0; g < 4; ++g) {
+              const int chunk = (wn * WN + 32 * j + 8 * g) >> 3;
+              const u32x2 v = *reinterpret_cast<const u32x2*>(row + ((chunk ^ lds_swizzle_k(kr)) << 4));
+              acc[i][j][4 * g + 0] += diag_coef * __uint_as_float(v[0] << 16);
+              acc[i][j][4 * g + 1] += diag_coef * __uint_as_float(v[0] & 0xffff0000u);
+              acc[i][j][4 * g + 2] += diag_coef * __uint_as_float(v[1] << 16);
+              acc[i][j][4 * g + 3] += diag_coef * __uint_as_float(v[1] & 0xffff0000u);
+            }
+          } else {
+            const int kc0 = wn * WN + j * 32 - slab * BK;  // K column of the block's first column
+            if (kc0 < 0 || kc0 + 32 > BK) continue;
+            const unsigned char* row = st + rowp + i * 32 * ROW + h8;
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              acc[i][j][4 * g + e] += diag_coef * __uint_as_float((uint32_t)(uint16_t)v[e] << 16);
+            for (int g = 0; g < 4; ++g) {
+              const int chunk = (kc0 + 8 * g) >> 3;
+              const u32x2 v = *reinterpret_cast<const u32x2*>(row + ((chunk ^ sw) << 4));
+              acc[i][j][4 * g + 0] += diag_coef * __uint_as_float(v[0] << 16);
+              acc[i][j][4 * g + 1] += diag_coef * __uint_as_float(v[0] & 0xffff0000u);
+              acc[i][j][4 * g + 2] += diag_coef * __uint_as_float(v[1] << 16);
+              acc[i][j][4 * g + 3] += diag_coef * __uint_as_float(v[1] & 0xffff0000u);
+            }
           }
-      }
+        }
     };
     const int KT = K / BK;
     constexpr int PS = 2 * DPW;  // DMA instructions per wave per stage
@@ -449,46 +474,22 @@ struct EngineF32 {
   }
 };
 
-// Copies the 256 x 256 bf16 tile at G (row stride ld elements) into LDS, row
-// major with 512-byte rows, in one burst of DMA loads (16 per wave for 8
-// waves), then waits for it. An epilogue that reads an operand tile
-// element by element thus pays one memory latency per tile, not one per
-// accumulator group. The caller has synchronised the workgroup before (the
-// GEMM ring is free) and synchronises it again after its last LDS read.
-template <int NT>
-MUON_INLINE void stage_tile_bf16(const u16* G, int64_t ld, u16* smem) {
-  constexpr int NW = NT / 64, PER_WAVE = 128 / NW;  // 128 KB = 128 wave instructions
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint32_t base = (uint32_t)(uintptr_t)smem;
-#pragma unroll
-  for (int p = 0; p < PER_WAVE; ++p) {
-    const int ins = wave * PER_WAVE + p;             // two rows of 512 bytes each
-    const int row = ins * 2 + (lane >> 5), ch = lane & 31;
-    dma16(G + row * ld + ch * 8, __builtin_amdgcn_readfirstlane(base + ins * 1024));
-  }
-  wait_vmcnt<0>();
-  __syncthreads();
-}
-
-MUON_INLINE float lds_tile_bf16(const u16* smem, int64_t r, int64_t c) {
-  return bf16_to_f32(smem[r * 256 + c]);
-}
-
 // ------------------------------------------------------------ phase epilogues
 //
-// Every epilogue walks the accumulators in groups of four consecutive rows of
-// one column: rows row0..row0+3 of column col.
+// fp32 engine: the epilogue walks the accumulators in groups of four
+// consecutive rows of one column and stores straight from them.
 //
-// bf16 engines (kStageTile): the epilogue computes the output values in place
-// in the accumulators. It then writes them through LDS, once per output
-// orientation. A 256 x 256 bf16 tile goes to LDS (2-byte writes for the
-// normal orientation, 8-byte writes for the transposed one), and then to
-// global memory in coalesced 16-byte stores, a whole 512-byte row per 32
-// lanes. The fp32 engine stores straight from the accumulators.
+// bf16 engines: a lane's accumulator group holds four consecutive columns of
+// one row. The epilogue scales the accumulators in place, writes the tile to
+// an LDS staging tile as bf16 (one 8-byte write per group), and then copies
+// the staging tile to global memory in coalesced 16-byte stores, once per
+// output orientation. Entries outside the matrix are zeroed in LDS; only tiles
+// on the matrix edge need that pass.
 
 template <class E>
 struct TileWalk {
-  // Calls f(row0, col, v[4]) for every 4-row group of the tile at (tile_r, tile_c).
+  // fp32 engine layout. Calls f(row0, col, v[4]) for every 4-row group of the
+  // tile at (tile_r, tile_c).
   template <class F>
   static MUON_INLINE void each(int64_t tile_r, int64_t tile_c, f32x16 (&acc)[E::FM][E::FN], F&& f) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -505,29 +506,23 @@ struct TileWalk {
           f(wr + i * 32 + 8 * g, wc + j * 32, v);
         }
   }
-  // Same walk; f may change v, and the result goes back into the accumulators.
-  template <class F>
-  static MUON_INLINE void apply(int64_t tile_r, int64_t tile_c, f32x16 (&acc)[E::FM][E::FN], F&& f) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t wr = tile_r + E::wave_m(wave) * E::WM + 4 * (lane >> 5);
-    const int64_t wc = tile_c + E::wave_n(wave) * E::WN + (lane & 31);
+  // Multiplies every accumulator by s.
+  static MUON_INLINE void scale(f32x16 (&acc)[E::FM][E::FN], float s) {
 #pragma unroll
     for (int i = 0; i < E::FM; ++i)
 #pragma unroll
       for (int j = 0; j < E::FN; ++j)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                        acc[i][j][4 * g + 3]};
-          f(wr + i * 32 + 8 * g, wc + j * 32, v);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) acc[i][j][4 * g + q] = v[q];
-          // One 32 x 32 block at a time: keeps the compiler from hoisting
-          // every load of the walk ahead of the arithmetic (register spills).
-          if (g == 3) __builtin_amdgcn_sched_barrier(0);
-        }
+        for (int e = 0; e < 16; ++e) acc[i][j][e] *= s;
   }
 };
+
+// Valid extent of a tile at (tr, tc) of an m x n matrix, in tile-local rows
+// and columns (at most BM x BN).
+template <class E>
+MUON_INLINE int tile_rows(int64_t tr, int m) { return (int)(m - tr < E::BM ? m - tr : E::BM); }
+template <class E>
+MUON_INLINE int tile_cols(int64_t tc, int n) { return (int)(n - tc < E::BN ? n - tc : E::BN); }
 
 // Stores a symmetric m x m result tile straight from the accumulators:
 // C[row][col] and the mirror C[col][row] (off-diagonal tiles only). Entries
@@ -543,82 +538,125 @@ MUON_INLINE void store_sym(T* C, int64_t ld, int m, bool mirror, int64_t row0, i
   if (mirror) Vec4<T>::store(C + col * ld + row0, v);
 }
 
-// Output staging tile: 256 rows of 256 bf16, padded to 528 bytes so that the
-// two 64-byte halves a wave writes per row group fall on different banks.
-constexpr int kOutStride = 528;
+// Output staging tile: 256 rows of 256 bf16 (512 bytes each), in 8-byte units
+// of four columns. Unit u of row r is stored at unit u ^ stage_swz(r) of that
+// row. stage_swz is a bijection of r % 32 chosen so that the three access
+// patterns below hit distinct banks, for 32- and for 64-bank LDS:
+//  - the accumulator writes: 32 consecutive rows, one unit;
+//  - row reads: one row, 16 bytes per lane;
+//  - transposing reads: 4 consecutive rows by 4 consecutive units per 16
+//    lanes, two such groups 8 rows apart per 32 lanes.
+constexpr int kOutStride = 512;
 constexpr int kOutBytes = 256 * kOutStride;
 
-MUON_INLINE uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+MUON_INLINE int stage_swz(int r) {
+  return ((r >> 2) & 1) | (((r >> 3) & 1) << 1) | ((r & 3) << 2) | ((((r >> 3) ^ (r >> 4)) & 1) << 4);
+}
+MUON_INLINE int stage_off(int r, int u) { return r * kOutStride + ((u ^ stage_swz(r)) << 3); }
+
+MUON_INLINE u32x4 bf16x8_bits(v4i16 lo, v4i16 hi) {
+  return __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// Accumulator tile -> LDS staging tile as bf16, in the normal (row r, col c)
-// or the transposed (row c, col r) orientation.
+// Columns 8ch .. 8ch+7 of staging row r. The two units of the chunk sit in one
+// 16-byte slot, swapped when stage_swz(r) is odd.
+MUON_INLINE u32x4 stage_read_row8(const unsigned char* smem, int r, int ch) {
+  const int sw = stage_swz(r);
+  const u32x4 v = *reinterpret_cast<const u32x4*>(smem + r * kOutStride + ((ch ^ (sw >> 1)) << 4));
+  if (sw & 1) return u32x4{v[2], v[3], v[0], v[1]};
+  return v;
+}
+
+// Transposing read. In each group of 16 lanes, lane i receives rows
+// r0 .. r0+7 of column c0 + i, where c0 is a multiple of 16 and r0 a multiple
+// of 8 (both uniform over the group). Lane i addresses row r0 + i/4 (and
+// r0 + 4 + i/4), unit c0/4 + i%4.
+MUON_INLINE u32x4 stage_read_col8(const unsigned char* smem, int r0, int c0) {
+  const int i = threadIdx.x & 15;
+  const int u = (c0 >> 2) + (i & 3);
+  const v4i16 lo = lds_read_tr(smem + stage_off(r0 + (i >> 2), u));
+  const v4i16 hi = lds_read_tr(smem + stage_off(r0 + 4 + (i >> 2), u));
+  return bf16x8_bits(lo, hi);
+}
+
+// bf16 accumulator tile -> staging tile. Lane l's group (i, j, g) holds row
+// wm*WM + 32i + l%32, columns wn*WN + 32j + 8g + 4(l/32) .. +3: one unit.
 template <class E>
-MUON_INLINE void acc_to_lds(f32x16 (&acc)[E::FM][E::FN], unsigned char* smem, bool transposed) {
+MUON_INLINE void acc_to_lds(f32x16 (&acc)[E::FM][E::FN], unsigned char* smem) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wr = E::wave_m(wave) * E::WM + 4 * (lane >> 5);
-  const int wc = E::wave_n(wave) * E::WN + (lane & 31);
+  const int wr = E::wave_m(wave) * E::WM + (lane & 31);
+  const int wu = E::wave_n(wave) * (E::WN / 4) + (lane >> 5);
 #pragma unroll
   for (int i = 0; i < E::FM; ++i)
 #pragma unroll
     for (int j = 0; j < E::FN; ++j)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int r0 = wr + i * 32 + 8 * g, c = wc + j * 32;
-        if (transposed) {
-          u32x2 t;
-          t[0] = pack_bf16x2(acc[i][j][4 * g], acc[i][j][4 * g + 1]);
-          t[1] = pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
-          *reinterpret_cast<u32x2*>(smem + c * kOutStride + r0 * 2) = t;
-        } else {
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            *reinterpret_cast<u16*>(smem + (r0 + q) * kOutStride + c * 2) = f32_to_bf16(acc[i][j][4 * g + q]);
-        }
+        u32x2 t;
+        t[0] = pack_bf16x2(acc[i][j][4 * g], acc[i][j][4 * g + 1]);
+        t[1] = pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+        *reinterpret_cast<u32x2*>(smem + stage_off(wr + 32 * i, wu + 8 * j + 2 * g)) = t;
       }
 }
 
-// LDS staging tile -> the 256 x 256 tile of a bf16 matrix whose origin is dst
-// (row stride ld elements), in 16-byte stores.
+// Zeroes the staging entries at rows >= rl or columns >= cl. Called between
+// two barriers, for edge tiles only.
+template <int NT>
+MUON_INLINE void mask_lds(unsigned char* smem, int rl, int cl) {
+#pragma unroll 1
+  for (int p = 0; p < 256 * 64 / NT; ++p) {
+    const int idx = threadIdx.x + p * NT, r = idx >> 6, u = idx & 63;
+    const int keep = r < rl ? cl - 4 * u : 0;  // valid columns in this unit
+    if (keep >= 4) continue;
+    u32x2* q = reinterpret_cast<u32x2*>(smem + stage_off(r, u));
+    u32x2 v = *q;
+    if (keep <= 0) { v[0] = 0u; v[1] = 0u; }
+    else if (keep == 1) { v[0] &= 0xffffu; v[1] = 0u; }
+    else if (keep == 2) { v[1] = 0u; }
+    else { v[1] &= 0xffffu; }
+    *q = v;
+  }
+}
+
+// Staging tile -> the 256 x 256 tile at dst (row stride ld): 32 lanes per row.
 template <int NT>
 MUON_INLINE void lds_to_global(const unsigned char* smem, u16* dst, int64_t ld) {
 #pragma unroll 2
   for (int p = 0; p < 256 * 32 / NT; ++p) {
     const int idx = threadIdx.x + p * NT, row = idx >> 5, ch = idx & 31;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(smem + row * kOutStride + ch * 16);
-    *((g_u32x4*)(dst + row * ld + ch * 8)) = v;
+    *((g_u32x4*)(dst + row * ld + ch * 8)) = stage_read_row8(smem, row, ch);
   }
 }
 
-// LDS staging tile -> the transpose of the tile at dst_t: row c of dst_t gets
-// column c of the staging tile. A lane gathers 8 consecutive rows of one
-// column (2-byte LDS reads; a wave reads 64 adjacent columns of one row at a
-// time) and stores them as one 16-byte chunk.
+// Staging tile -> the transpose of the tile at dst_t: row c of dst_t gets
+// column c of the staging tile. Wave task t covers columns 16(t%16) .. +15 and
+// rows 32(t/16) .. +31; its 4 lane groups take 8 rows each, so every dst_t row
+// receives 64 contiguous bytes per store instruction.
 template <int NT>
 MUON_INLINE void lds_to_global_t(const unsigned char* smem, u16* dst_t, int64_t ld_t) {
-  const int c = threadIdx.x & 255;
+  constexpr int NW = NT / 64;
+  const int wave = threadIdx.x >> 6, G = (threadIdx.x >> 4) & 3, i = threadIdx.x & 15;
 #pragma unroll 2
-  for (int p = 0; p < 256 * 32 / NT; ++p) {
-    const int r0 = 8 * ((threadIdx.x >> 8) + p * (NT / 256));
-    const unsigned char* col = smem + r0 * kOutStride + c * 2;
-    u32x4 v;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      v[e] = (uint32_t)*reinterpret_cast<const u16*>(col + (2 * e) * kOutStride) |
-             ((uint32_t)*reinterpret_cast<const u16*>(col + (2 * e + 1) * kOutStride) << 16);
-    *((g_u32x4*)(dst_t + c * ld_t + r0)) = v;
+  for (int p = 0; p < 128 / NW; ++p) {
+    const int t = wave + p * NW;
+    const int c0 = 16 * (t & 15), r0 = 32 * (t >> 4) + 8 * G;
+    *((g_u32x4*)(dst_t + (c0 + i) * ld_t + r0)) = stage_read_col8(smem, r0, c0);
   }
 }
 
-// Writes the (masked) accumulator tile to dst and, if dst_t is set, its
-// transpose to dst_t, through one LDS staging pass. LDS must be free on entry;
+// Writes the accumulator tile, scaled beforehand, to dst and, if dst_t is
+// set, its transpose to dst_t, through one staging pass. Entries outside the
+// first rl rows and cl columns are written as 0. LDS must be free on entry;
 // it is free again on exit.
 template <class E>
-MUON_INLINE void store_tile_staged(f32x16 (&acc)[E::FM][E::FN], unsigned char* smem, u16* dst, int64_t ld,
-                                   u16* dst_t, int64_t ld_t) {
-  acc_to_lds<E>(acc, smem, false);
+MUON_INLINE void store_tile_staged(f32x16 (&acc)[E::FM][E::FN], unsigned char* smem, int rl, int cl,
+                                   u16* dst, int64_t ld, u16* dst_t, int64_t ld_t) {
+  acc_to_lds<E>(acc, smem);
   __syncthreads();
+  if (rl < E::BM || cl < E::BN) {
+    mask_lds<E::NT>(smem, rl, cl);
+    __syncthreads();
+  }
   lds_to_global<E::NT>(smem, dst, ld);
   if (dst_t) lds_to_global_t<E::NT>(smem, dst_t, ld_t);
   __syncthreads();
@@ -642,11 +680,9 @@ MUON_INLINE void gram_tile(const PhaseArgs& args, const MatDev& d, int ti, int t
   const int64_t tr = (int64_t)ti * E::BM, tc = (int64_t)tj * E::BN;
   const int m = d.m;
   if constexpr (E::kStageTile) {
-    TileWalk<E>::apply(tr, tc, acc, [&](int64_t row0, int64_t col, float v[4]) __attribute__((always_inline)) {
-      for (int q = 0; q < 4; ++q) v[q] = (col < m && row0 + q < m) ? v[q] * alpha : 0.f;
-    });
-    store_tile_staged<E>(acc, static_cast<unsigned char*>(smem), A + tr * d.lda + tc, d.lda,
-                         mirror ? A + tc * d.lda + tr : nullptr, d.lda);
+    if (alpha != 1.f) TileWalk<E>::scale(acc, alpha);
+    store_tile_staged<E>(acc, static_cast<unsigned char*>(smem), tile_rows<E>(tr, m), tile_cols<E>(tc, m),
+                         A + tr * d.lda + tc, d.lda, mirror ? A + tc * d.lda + tr : nullptr, d.lda);
   } else {
     TileWalk<E>::each(tr, tc, acc, [&](int64_t row0, int64_t col, float v[4]) __attribute__((always_inline)) {
       for (int q = 0; q < 4; ++q) v[q] *= alpha;
@@ -655,31 +691,51 @@ MUON_INLINE void gram_tile(const PhaseArgs& args, const MatDev& d, int ti, int t
   }
 }
 
+// B = b*A when c = 0: no product, the tile and its mirror are scaled
+// elementwise, 16 bytes per lane.
+template <int NT>
+MUON_INLINE void scale_tile_pair(const u16* A, u16* B, int64_t ld, int64_t tr, int64_t tc, bool mirror,
+                                 float cb) {
+#pragma unroll 1
+  for (int p = 0; p < 256 * 32 / NT; ++p) {
+    const int idx = threadIdx.x + p * NT, row = idx >> 5, ch = idx & 31;
+#pragma unroll 1
+    for (int s = 0; s < (mirror ? 2 : 1); ++s) {
+      const int64_t o = (s ? (tc + row) * ld + tr : (tr + row) * ld + tc) + ch * 8;
+      u32x4 v = *((const g_u32x4*)(A + o));
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        v[e] = pack_bf16x2(cb * __uint_as_float(v[e] << 16), cb * __uint_as_float(v[e] & 0xffff0000u));
+      *((g_u32x4*)(B + o)) = v;
+    }
+  }
+}
+
 template <class E>
 MUON_INLINE void square_tile(const PhaseArgs& args, const MatDev& d, int ti, int tj, void* smem) {
   typedef typename E::T T;
   const T* A = static_cast<const T*>(d.a);
-  f32x16 acc[E::FM][E::FN];
-  E::run(A + (int64_t)ti * E::BM * d.lda, d.lda, A + (int64_t)tj * E::BN * d.lda, d.lda, d.mp,
-         static_cast<T*>(smem), acc);
   T* B = static_cast<T*>(d.b);
   const float cb = args.co.b, cc = args.co.c;
   const bool mirror = ti != tj;
   const int64_t tr = (int64_t)ti * E::BM, tc = (int64_t)tj * E::BN;
   const int m = d.m;
   if constexpr (E::kStageTile) {
-    // B = b*A + c*(A*A), formed in fp32 and rounded once.
-    stage_tile_bf16<E::NT>(A + tr * d.lda + tc, d.lda, static_cast<T*>(smem));
-    TileWalk<E>::apply(tr, tc, acc, [&](int64_t row0, int64_t col, float v[4]) __attribute__((always_inline)) {
-      for (int q = 0; q < 4; ++q) {
-        const float aij = lds_tile_bf16(static_cast<const u16*>(smem), row0 + q - tr, col - tc);
-        v[q] = (col < m && row0 + q < m) ? cb * aij + cc * v[q] : 0.f;
-      }
-    });
-    __syncthreads();  // every wave is done with the staged A tile
-    store_tile_staged<E>(acc, static_cast<unsigned char*>(smem), B + tr * d.lda + tc, d.lda,
-                         mirror ? B + tc * d.lda + tr : nullptr, d.lda);
+    if (cc == 0.f) {
+      scale_tile_pair<E::NT>(A, B, d.lda, tr, tc, mirror, cb);
+      return;
+    }
+    // B = c * (A*A + (b/c)*A). The engine adds (b/c)*A[i][j] while the K
+    // steps over the tile's columns, which hold A[i][j], are in LDS.
+    f32x16 acc[E::FM][E::FN];
+    E::run(A + tr * d.lda, d.lda, A + tc * d.lda, d.lda, d.mp, static_cast<T*>(smem), acc,
+           tj * (E::BN / E::BK), cb / cc);
+    TileWalk<E>::scale(acc, cc);
+    store_tile_staged<E>(acc, static_cast<unsigned char*>(smem), tile_rows<E>(tr, m), tile_cols<E>(tc, m),
+                         B + tr * d.lda + tc, d.lda, mirror ? B + tc * d.lda + tr : nullptr, d.lda);
   } else {
+    f32x16 acc[E::FM][E::FN];
+    E::run(A + tr * d.lda, d.lda, A + tc * d.lda, d.lda, d.mp, static_cast<T*>(smem), acc);
     TileWalk<E>::each(tr, tc, acc, [&](int64_t row0, int64_t col, float v[4]) __attribute__((always_inline)) {
       for (int q = 0; q < 4; ++q) v[q] = cb * Elem<T>::load(A + (row0 + q) * d.lda + col) + cc * v[q];
       store_sym<T>(B, d.lda, m, mirror, row0, col, v);
@@ -687,51 +743,70 @@ MUON_INLINE void square_tile(const PhaseArgs& args, const MatDev& d, int ti, int
   }
 }
 
-// Last-iteration weight update through the staging tile: O (already in LDS
-// as bf16, in W's orientation) is applied to the W tile with origin
-// (wr0, wc0), 8 consecutive W elements per lane. W' = W - lr*scale*O and
-// delta = -lr*scale*O, each rounded once. Full, 16-byte aligned groups use
-// vector accesses; ragged or unaligned ones go element by element.
-template <int NT>
-MUON_INLINE void apply_from_lds(const unsigned char* smem, const MatDev& d, int64_t wr0, int64_t wc0) {
+// Last-iteration weight update of 8 consecutive W elements (row gr, columns
+// gc .. gc+7, clipped to the matrix) from the bf16 O values in o:
+// W' = W - lr*scale*O and delta = -lr*scale*O, each rounded once. A full,
+// 16-byte aligned group uses vector accesses; a ragged or unaligned one goes
+// element by element.
+MUON_INLINE void apply8(const MatDev& d, int64_t gr, int64_t gc, u32x4 ov) {
   u16* W = static_cast<u16*>(d.w);
   u16* D = static_cast<u16*>(d.delta);
   const float ls = d.lr_scale;
-  const int64_t R = d.rows, C = d.cols;
-#pragma unroll 1
-  for (int p = 0; p < 256 * 32 / NT; ++p) {
-    const int idx = threadIdx.x + p * NT, row = idx >> 5, ch = idx & 31;
-    const int64_t gr = wr0 + row, gc = wc0 + ch * 8;
-    if (gr >= R || gc >= C) continue;
-    const u32x4 ov = *reinterpret_cast<const u32x4*>(smem + row * kOutStride + ch * 16);
-    float o[8];
+  const int64_t C = d.cols;
+  float o[8];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      o[2 * e] = __uint_as_float(ov[e] << 16);
-      o[2 * e + 1] = __uint_as_float(ov[e] & 0xffff0000u);
+  for (int e = 0; e < 4; ++e) {
+    o[2 * e] = __uint_as_float(ov[e] << 16);
+    o[2 * e + 1] = __uint_as_float(ov[e] & 0xffff0000u);
+  }
+  const int64_t base = gr * C + gc;
+  if (gc + 8 <= C && (base & 7) == 0) {
+    if (W) {
+      u32x4 wv = *((const g_u32x4*)(W + base));
+      u32x4 nv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        nv[e] = pack_bf16x2(__uint_as_float(wv[e] << 16) - ls * o[2 * e],
+                            __uint_as_float(wv[e] & 0xffff0000u) - ls * o[2 * e + 1]);
+      *((g_u32x4*)(W + base)) = nv;
     }
-    const int64_t base = gr * C + gc;
-    if (gc + 8 <= C && (base & 7) == 0) {
-      if (W) {
-        u32x4 wv = *((const g_u32x4*)(W + base));
-        u32x4 nv;
+    if (D) {
+      u32x4 dv;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          nv[e] = pack_bf16x2(__uint_as_float(wv[e] << 16) - ls * o[2 * e],
-                              __uint_as_float(wv[e] & 0xffff0000u) - ls * o[2 * e + 1]);
-        *((g_u32x4*)(W + base)) = nv;
-      }
-      if (D) {
-        u32x4 dv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dv[e] = pack_bf16x2(-ls * o[2 * e], -ls * o[2 * e + 1]);
-        *((g_u32x4*)(D + base)) = dv;
-      }
-    } else {
-      for (int e = 0; e < 8 && gc + e < C; ++e) {
-        if (W) Elem<u16>::store(W + base + e, Elem<u16>::load(W + base + e) - ls * o[e]);
-        if (D) Elem<u16>::store(D + base + e, -ls * o[e]);
-      }
+      for (int e = 0; e < 4; ++e) dv[e] = pack_bf16x2(-ls * o[2 * e], -ls * o[2 * e + 1]);
+      *((g_u32x4*)(D + base)) = dv;
+    }
+  } else {
+    for (int e = 0; e < 8 && gc + e < C; ++e) {
+      if (W) Elem<u16>::store(W + base + e, Elem<u16>::load(W + base + e) - ls * o[e]);
+      if (D) Elem<u16>::store(D + base + e, -ls * o[e]);
+    }
+  }
+}
+
+// Last iteration: the staging tile holds the X tile at (tr, tc). O = X for a
+// wide matrix (W tile at (tr, tc), read by rows), O = X^T for a tall one (W
+// tile at (tc, tr), read by columns).
+template <int NT>
+MUON_INLINE void apply_from_lds(const unsigned char* smem, const MatDev& d, int64_t tr, int64_t tc) {
+  const int64_t R = d.rows, C = d.cols;
+  if (!d.tall) {
+#pragma unroll 1
+    for (int p = 0; p < 256 * 32 / NT; ++p) {
+      const int idx = threadIdx.x + p * NT, row = idx >> 5, ch = idx & 31;
+      const int64_t gr = tr + row, gc = tc + ch * 8;
+      if (gr < R && gc < C) apply8(d, gr, gc, stage_read_row8(smem, row, ch));
+    }
+  } else {
+    constexpr int NW = NT / 64;
+    const int wave = threadIdx.x >> 6, G = (threadIdx.x >> 4) & 3, i = threadIdx.x & 15;
+#pragma unroll 1
+    for (int p = 0; p < 128 / NW; ++p) {
+      const int t = wave + p * NW;
+      const int c0 = 16 * (t & 15), r0 = 32 * (t >> 4) + 8 * G;
+      const u32x4 v = stage_read_col8(smem, r0, c0);  // every lane takes part
+      const int64_t gr = tc + c0 + i, gc = tr + r0;
+      if (gr < R && gc < C) apply8(d, gr, gc, v);
     }
   }
 }
@@ -756,17 +831,15 @@ MUON_INLINE void update_tile(const PhaseArgs& args, const MatDev& d, int ti, int
   const int m = d.m, n = d.n;
   if constexpr (E::kStageTile) {
     // acc already holds a*X + B*X.
-    TileWalk<E>::apply(tr, tc, acc, [&](int64_t row0, int64_t col, float v[4]) __attribute__((always_inline)) {
-      for (int q = 0; q < 4; ++q) v[q] = (col < n && row0 + q < m) ? xs * v[q] : 0.f;
-    });
+    if (xs != 1.f) TileWalk<E>::scale(acc, xs);
     unsigned char* sm = static_cast<unsigned char*>(smem);
     if constexpr (!LAST) {
-      store_tile_staged<E>(acc, sm, static_cast<T*>(d.x[dst]) + tr * d.ldx + tc, d.ldx, nullptr, 0);
+      store_tile_staged<E>(acc, sm, tile_rows<E>(tr, m), tile_cols<E>(tc, n),
+                           static_cast<T*>(d.x[dst]) + tr * d.ldx + tc, d.ldx, nullptr, 0);
     } else {
-      // O = X_T, or X_T^T for a tall matrix: stage O in W's orientation.
-      acc_to_lds<E>(acc, sm, d.tall != 0);
+      acc_to_lds<E>(acc, sm);
       __syncthreads();
-      apply_from_lds<E::NT>(sm, d, d.tall ? tc : tr, d.tall ? tr : tc);
+      apply_from_lds<E::NT>(sm, d, tr, tc);
       __syncthreads();
     }
     return;

@@ -62,6 +62,39 @@ def test_without_nesterov(dtype):
     run_case(w, f"nesterov=False {dtype}")
 
 
+@pytest.mark.parametrize("coeffs", [(1.5, -0.5, 0.0), (2.0, -1.5, 0.5)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_other_polynomial_coefficients(dtype, coeffs):
+    """The step for any (a, b, c). c = 0 is the cubic iteration, where B = b*A
+    needs no product; c != 0 folds b*A into the A*A product."""
+    w = wl.custom_workload(f"coeffs_{dtype}", [(384, 640), (640, 384), (300, 300)], dtype,
+                           seed=35, ns_steps=4)
+    inputs = wl.generate(w)
+    hp = dict(w.hparams(), coeffs=coeffs)
+    log(f"case coeffs={coeffs} {dtype}")
+    gpu = gpu_step(inputs, dtype, hp)
+    want = oracle_step(inputs, dtype, hp)
+    compare(gpu, want, dtype, hp, inputs, f"coeffs={coeffs} {dtype}")
+
+
+def test_bf16_stores_round_to_nearest_even():
+    """M' = beta*M + G is formed in fp32 and stored once as bf16. Every stored
+    value must be the nearest-even bf16 of the fp32 value, whether the fp32
+    value was formed with one rounding (fused) or two."""
+    shapes = [(512, 768), (333, 200)]
+    w = wl.custom_workload("rne", shapes, "bf16", seed=37, ns_steps=0, g_std=1.0)
+    inputs = wl.generate(w)
+    gpu = gpu_step(inputs, "bf16", w.hparams())
+    beta = np.float32(w.beta)
+    for (Wg, Mg, Dg), (W, G, M) in zip(gpu, inputs):
+        g = wl.bf16_bits_to_f32(G)
+        m = wl.bf16_bits_to_f32(M)
+        fused = (beta.astype(np.float64) * m.astype(np.float64) + g.astype(np.float64)).astype(np.float32)
+        split = (beta * m + g).astype(np.float32)
+        ok = (Mg == wl.f32_to_bf16_bits(fused)) | (Mg == wl.f32_to_bf16_bits(split))
+        assert ok.all(), f"{int((~ok).sum())} of {ok.size} M' values are not RNE of beta*M + G"
+
+
 def test_zero_gradient_and_momentum_give_zero_update():
     shapes = [(300, 500), (500, 300)]
     inputs = [(wl.to_storage(wl.draw(5, i, 1, s, 0.02), "bf16"),
