@@ -31,6 +31,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "muon_internal.h"
 
 namespace muon {
@@ -240,13 +242,21 @@ struct EngineBF16 {
       }
     }
     const int64_t qstep = QK ? (int64_t)BK * ldq : BK;  // Q elements per K step
+    // The K loop starts at the diagonal window (if any) and wraps around:
+    // loop step kt reads operand K step (kt + kt0) mod KT. The window is then
+    // the first BM/BK steps, and the steady-state loop carries no diagonal
+    // code.
+    const int KT = K / BK;
+    const int kt0 = diag_kt0 >= 0 ? diag_kt0 : 0;
     auto issue = [&](int kt) __attribute__((always_inline)) {
       const uint32_t st = lds_base + (kt % STAGES) * STAGE_BYTES;
+      int ks = kt + kt0;
+      if (ks >= KT) ks -= KT;
 #pragma unroll
       for (int p = 0; p < DPW; ++p) {
         const uint32_t off = (wave * DPW + p) * 1024;
-        dma16(gp[p] + kt * BK, __builtin_amdgcn_readfirstlane(st + off));
-        dma16(gq[p] + kt * qstep, __builtin_amdgcn_readfirstlane(st + OP_BYTES + off));
+        dma16(gp[p] + ks * BK, __builtin_amdgcn_readfirstlane(st + off));
+        dma16(gq[p] + ks * qstep, __builtin_amdgcn_readfirstlane(st + OP_BYTES + off));
       }
     };
     // P fragment reads: lane l reads row l % 32 of each 32-row block, 16-byte
@@ -293,15 +303,14 @@ struct EngineBF16 {
         for (int j = 0; j < FN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fq[buf][j], fp[buf][i], acc[i][j], 0, 0, 0);
     };
-    // Diagonal window: K steps diag_kt0 .. diag_kt0 + BM/BK - 1 (slab =
-    // kt - diag_kt0) hold the output tile's own rows (QK: Q's K rows) or
+    // Diagonal window: loop steps slab = 0 .. BM/BK - 1 (operand K steps
+    // diag_kt0 + slab) hold the output tile's own rows (QK: Q's K rows) or
     // columns (otherwise: P's K columns) slab*BK .. +BK. Accumulator group
     // (i, j, g) of lane l holds row R = wm*WM + 32i + l%32, columns
     // C .. C+3 with C = wn*WN + 32j + 8g + 4(l/32): one 8-byte read of the
     // operand row R - slab*BK (QK) or of P row R at K column C - slab*BK.
     auto diag_add = [&](int kt) __attribute__((always_inline)) {
-      const int slab = kt - diag_kt0;
-      if (diag_kt0 < 0 || slab < 0 || slab >= BM / BK) return;
+      const int slab = kt;
       const unsigned char* st = sb + (kt % STAGES) * STAGE_BYTES;
       const int h8 = 8 * h;
 #pragma unroll
@@ -338,7 +347,6 @@ struct EngineBF16 {
           }
         }
     };
-    const int KT = K / BK;
     constexpr int PS = 2 * DPW;  // DMA instructions per wave per stage
     // Waits until this wave's loads of stage j are done: at most the loads of
     // the later stages already issued, min(STAGES - 2, KT - 1 - j) of them,
@@ -357,8 +365,7 @@ struct EngineBF16 {
     __syncthreads();
     if (STAGES - 1 < KT) issue(STAGES - 1);
     read_frags(0, 0, 0);
-    for (int kt = 0; kt < KT - 1; ++kt) {
-      diag_add(kt);
+    auto step = [&](int kt) __attribute__((always_inline)) {
 #pragma unroll
       for (int kk = 0; kk < KK - 1; ++kk) {
         read_frags((kk + 1) & 1, kt, kk + 1);
@@ -376,8 +383,15 @@ struct EngineBF16 {
       __builtin_amdgcn_sched_barrier(0);
       if (kt + STAGES < KT) issue(kt + STAGES);
       read_frags(0, kt + 1, 0);
+    };
+    const int window = diag_kt0 >= 0 ? BM / BK : 0;
+    int kt = 0;
+    for (; kt < window && kt < KT - 1; ++kt) {
+      diag_add(kt);
+      step(kt);
     }
-    diag_add(KT - 1);
+    for (; kt < KT - 1; ++kt) step(kt);
+    if (KT - 1 < window) diag_add(KT - 1);
 #pragma unroll
     for (int kk = 0; kk < KK - 1; ++kk) {
       read_frags((kk + 1) & 1, KT - 1, kk + 1);
@@ -386,6 +400,256 @@ struct EngineBF16 {
     mfmas((KK - 1) & 1);
     // Every wave is done with the ring before the next tile's first loads.
     __syncthreads();
+  }
+};
+
+// Direct global -> LDS copy of 16 bytes per lane, addressed as a uniform
+// 64-bit base plus a per-lane 32-bit byte offset (the saddr form of
+// global_load_lds_dwordx4). Same M0 handling as dma16.
+MUON_INLINE void dma16s(const void* base_, uint32_t voff, uint32_t lds) {
+  // The base must live in SGPRs; read it from the first lane (it is
+  // uniform). readfirstlane returns int: each half goes through uint32_t so
+  // that the low half is zero-extended, not sign-extended, into 64 bits.
+  const uint64_t b = (uint64_t)(uintptr_t)base_;
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint64_t base = ((uint64_t)hi << 32) | (uint64_t)lo;
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(base), "s"(__builtin_amdgcn_readfirstlane(lds))
+      : "memory");
+}
+
+// Four-wave bf16 engine: 2 x 2 waves of 128 x 128 each (accumulators in the
+// AGPR half of the register file), K step 64, a ring of 2 LDS stages.
+//
+// With one wave per SIMD nothing else hides a stalled instruction stream, so
+// the loop issues MFMAs one at a time with the rest of the work between
+// them: while MFMA n of a sub-step runs, the wave reads fragment n of the
+// next sub-step (n < 8) and, in sub-step 0, issues DMA instruction n of the
+// next K step. Larger wave tiles read a third less LDS per flop than the
+// eight-wave layout; on a power-capped chip that is worth more than the
+// latency the second wave per SIMD would hide.
+//
+// The operand layouts, the swizzles, the accumulator layout, the diagonal
+// window and the rotated K order are those of EngineBF16.
+template <bool QK>
+struct Engine4 {
+  typedef u16 T;
+  static constexpr int BM = 256, BN = 256, BK = 64, STAGES = 2;
+  static constexpr int NT = 256, NW = 4;
+  static constexpr int WM = 128, WN = 128, FM = 4, FN = 4;
+  static constexpr int S = 8, ROW = 128;             // P rows of 64 bf16
+  static constexpr int OP_BYTES = BM * ROW;          // 32 KB per operand and stage
+  static constexpr int STAGE_BYTES = 2 * OP_BYTES;
+  static constexpr int DPW = OP_BYTES / 1024 / NW;   // 8 DMA instructions per wave and operand
+  static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+  static constexpr bool kStageTile = true;
+  static constexpr bool kQK = QK;
+  static MUON_INLINE int wave_m(int w) { return w >> 1; }
+  static MUON_INLINE int wave_n(int w) { return w & 1; }
+
+  static MUON_INLINE void run(const u16* __restrict__ P, int64_t ldp, const u16* __restrict__ Q,
+                              int64_t ldq, int K, u16* smem, f32x16 (&acc)[FM][FN],
+                              int diag_kt0 = -1, float diag_coef = 0.f) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave_m(wave), wn = wave_n(wave);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    const int KT = K / BK;
+    const int kt0 = diag_kt0 >= 0 ? diag_kt0 : 0;
+    // DMA plan. Instruction p of this wave fills 1 KB of each operand: P rows
+    // 8(wave*DPW + p) .. +7 (lane l: row + l/8, slot l%8, global chunk
+    // slot ^ swz(row) = l%8 ^ l/8 ^ p%2), and Q likewise, or for QK the K rows
+    // 2(wave*DPW + p) .. +1 (lane l: row + l/32, slot l%32, global chunk
+    // slot ^ swzk(row), which depends on p%2 and l/32 only). The per-lane part
+    // of the address depends on p only through p%2: two offsets per operand.
+    uint32_t vp[2], vq[2];
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+      vp[par] = (uint32_t)((lane >> 3) * ldp * 2) + ((((lane & 7) ^ (lane >> 3) ^ par)) << 4);
+      if (QK)
+        vq[par] = (uint32_t)((lane >> 5) * ldq * 2) +
+                  (((lane & 31) ^ lds_swizzle_k(2 * par + (lane >> 5))) << 4);
+      else
+        vq[par] = (uint32_t)((lane >> 3) * ldq * 2) + ((((lane & 7) ^ (lane >> 3) ^ par)) << 4);
+    }
+    const uint32_t lds_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem);
+    // DMA instruction d (0 .. 2*DPW-1) of loop step kt: even d loads P, odd
+    // d loads Q, both for p = d/2.
+    auto dma = [&](int kt, int d) __attribute__((always_inline)) {
+      int ks = kt + kt0;
+      if (ks >= KT) ks -= KT;
+      const int p = d >> 1, row = wave * DPW + p;
+      const uint32_t st = lds_base + (kt & 1) * STAGE_BYTES + row * 1024;
+      if (d & 1) {
+        const u16* qb = QK ? Q + ((int64_t)ks * BK + 2 * row) * ldq : Q + (int64_t)(8 * row) * ldq + ks * BK;
+        dma16s(qb, vq[p & 1], st + OP_BYTES);
+      } else {
+        dma16s(P + (int64_t)(8 * row) * ldp + ks * BK, vp[p & 1], st);
+      }
+    };
+
+    // Fragment reads. P: lane l reads row l%32 of each 32-row block, 16-byte
+    // chunk 2*kk + l/32 at slot chunk ^ swz(row). Q (not QK): the same on Q
+    // rows. QK: two transposing reads per fragment, as in EngineBF16.
+    const int r32 = lane & 31, h = lane >> 5, sw = lds_swizzle<S>(r32);
+    const unsigned char* sb = reinterpret_cast<const unsigned char*>(smem);
+    const uint32_t rowp = (wm * WM + r32) * ROW, rowq = OP_BYTES + (wn * WN + r32) * ROW;
+    const int G = lane >> 4, i16 = lane & 15;
+    const uint32_t qrow = OP_BYTES + (8 * (G >> 1) + (i16 >> 2)) * 512;
+    uint32_t qcol[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int chunk = (wn * WN + 32 * j + 16 * (G & 1) + 4 * (i16 & 3)) >> 3;
+      qcol[j] = ((chunk ^ lds_swizzle_k(i16 >> 2)) << 4) + 8 * (i16 & 1);
+    }
+    bf16x8 fp[2][FM], fq[2][FN];
+    // Read item f (0..3: P block f, 4..7: Q block f-4) of sub-step kk of loop
+    // step kt into buffer buf.
+    auto rd = [&](int buf, int kt, int kk, int f) __attribute__((always_inline)) {
+      const unsigned char* st = sb + (kt & 1) * STAGE_BYTES;
+      const int fo = (((2 * kk) | h) ^ sw) * 16;
+      if (f < FM) {
+        fp[buf][f] = *reinterpret_cast<const bf16x8*>(st + rowp + f * 32 * ROW + fo);
+      } else if (QK) {
+        const unsigned char* q = st + qrow + kk * 16 * 512 + qcol[f - FM];
+        const v4i16 lo = lds_read_tr(q), hi = lds_read_tr(q + 4 * 512);
+        fq[buf][f - FM] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      } else {
+        fq[buf][f - FM] = *reinterpret_cast<const bf16x8*>(st + rowq + (f - FM) * 32 * ROW + fo);
+      }
+    };
+    // MFMA n (block i = n/4, j = n%4) on buffer buf: Q fragment first, so
+    // lane l%32 indexes output rows (the accumulator layout of EngineBF16).
+    auto mf = [&](int buf, int n) __attribute__((always_inline)) {
+      const int i = n >> 2, j = n & 3;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fq[buf][j], fp[buf][i], acc[i][j], 0, 0, 0);
+    };
+
+    // Diagonal window (loop steps 0 .. 3, when diag_kt0 >= 0): the term
+    // added is 1 * (the operand tile at the output tile's own rows or
+    // columns), and it is added by MFMAs against 0/1 selection fragments:
+    // I_t[c][k] = (c == 16t + k) for the 16 K values of a sub-step. Step
+    // slab holds output rows (QK) or columns slab*64 .. +63, owned by the
+    // waves with wm (QK) or wn equal to slab/2, in accumulator blocks
+    // 2*(slab%2) + kk/2. Sub-step kk covers 16 of them, half t = kk%2 of the
+    // block, and the fragments it already holds are the operand values:
+    //  - QK (update, X' = X + B X): fq[j] holds X[row][col] with the column
+    //    on lanes, so D += fq[j] * I_t^T adds X to block (2*(slab%2) + kk/2, j);
+    //  - otherwise (square, A' A' + A'): fp[i] holds P[row][k] with the row
+    //    on lanes, so D += I_t * fp[i] adds A' to block (i, 2*(slab%2) + kk/2).
+    // The diagonal coefficient must be 1 (diag_coef is not used).
+    bf16x8 sel[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        sel[t][e] = (__bf16)(r32 == 16 * t + 8 * h + e ? 1.f : 0.f);
+    (void)diag_coef;
+
+#define MUON_SB() __builtin_amdgcn_sched_barrier(0)
+    // One loop step kt. Fragments of sub-step 0 are in buffer 0 on entry; on
+    // exit those of step kt+1 are. Unless LAST, the step issues the loads of
+    // step kt+1 (K index taken mod KT, so always in bounds) and reads its first
+    // fragments. WIN >= 0: a diagonal-window step whose slab has parity WIN;
+    // the waves that do not own the slab add 0 (their selection fragments are
+    // zero), so every wave runs the same code.
+    auto kstep = [&](int kt, auto LAST_, auto WIN_) __attribute__((always_inline)) {
+      constexpr bool LAST = decltype(LAST_)::value;
+      constexpr int WIN = decltype(WIN_)::value;
+      bf16x8 ds[2];
+      if constexpr (WIN >= 0) {
+        const bool own = (kt >> 1) == (QK ? wm : wn);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const u32x4 z = {0u, 0u, 0u, 0u};
+          ds[t] = own ? sel[t] : __builtin_bit_cast(bf16x8, z);
+        }
+      }
+      auto diag = [&](int buf, int kk) __attribute__((always_inline)) {
+        if constexpr (WIN >= 0) {
+          const int blk = 2 * WIN + (kk >> 1);
+#pragma unroll
+          for (int o = 0; o < 4; ++o) {
+            if (QK) acc[blk][o] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fq[buf][o], ds[kk & 1], acc[blk][o], 0, 0, 0);
+            else acc[o][blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ds[kk & 1], fp[buf][o], acc[o][blk], 0, 0, 0);
+          }
+        }
+      };
+#pragma unroll
+      for (int kk = 0; kk < 3; ++kk) {
+        const int b = kk & 1;
+#pragma unroll
+        for (int n = 0; n < 16; ++n) {
+          mf(b, n);
+          if (n < 8) rd(b ^ 1, kt, kk + 1, n);
+          if (!LAST && kk == 0) dma(kt + 1, n);
+          MUON_SB();
+        }
+        diag(b, kk);
+        MUON_SB();
+      }
+      // Sub-step 3 (buffer 1): half the MFMAs, then wait for this wave's
+      // loads of the next step and the barrier (after it every wave's loads
+      // are in LDS and every wave is done with this step's stage), then the
+      // other half under the first reads of the next step.
+#pragma unroll
+      for (int n = 0; n < 8; ++n) { mf(1, n); MUON_SB(); }
+      if (!LAST) wait_vmcnt<0>();
+      __syncthreads();
+      MUON_SB();
+#pragma unroll
+      for (int n = 8; n < 16; ++n) {
+        mf(1, n);
+        if (!LAST) rd(0, kt + 1, 0, n - 8);
+        MUON_SB();
+      }
+      diag(1, 3);  // buffer 1 is intact: the reads above fill buffer 0
+      MUON_SB();
+    };
+#undef MUON_SB
+    using F_ = std::false_type;
+    using T_ = std::true_type;
+    using NOWIN = std::integral_constant<int, -1>;
+    using W0 = std::integral_constant<int, 0>;
+    using W1 = std::integral_constant<int, 1>;
+
+#pragma unroll
+    for (int d = 0; d < 2 * DPW; ++d) dma(0, d);
+    wait_vmcnt<0>();
+    __syncthreads();
+#pragma unroll
+    for (int f = 0; f < 8; ++f) rd(0, 0, 0, f);
+    // K >= BM, so KT >= 4 and the window is loop steps 0 .. 3.
+    int kt = 0;
+    if (diag_kt0 >= 0) {
+      kstep(0, F_{}, W0{});
+      kstep(1, F_{}, W1{});
+      kstep(2, F_{}, W0{});
+      kstep(3, F_{}, W1{});
+      kt = 4;
+    }
+    if (kt < KT) {
+      for (; kt < KT - 1; ++kt) kstep(kt, F_{}, NOWIN{});
+      kstep(KT - 1, T_{}, NOWIN{});
+    } else {
+      // KT == 4 with a window: step 3 loaded a stage nobody reads.
+      wait_vmcnt<0>();
+      __syncthreads();
+    }
+    // The final barrier of the last step leaves the ring free.
   }
 };
 
@@ -480,8 +744,8 @@ struct EngineF32 {
 // consecutive rows of one column and stores straight from them.
 //
 // bf16 engines: a lane's accumulator group holds four consecutive columns of
-// one row. The epilogue scales the accumulators in place, writes the tile to
-// an LDS staging tile as bf16 (one 8-byte write per group), and then copies
+// one row. The epilogue writes the scaled tile to an LDS staging tile as bf16
+// (one 8-byte write per group), and then copies
 // the staging tile to global memory in coalesced 16-byte stores, once per
 // output orientation. Entries outside the matrix are zeroed in LDS; only tiles
 // on the matrix edge need that pass.
@@ -505,15 +769,6 @@ struct TileWalk {
                         acc[i][j][4 * g + 3]};
           f(wr + i * 32 + 8 * g, wc + j * 32, v);
         }
-  }
-  // Multiplies every accumulator by s.
-  static MUON_INLINE void scale(f32x16 (&acc)[E::FM][E::FN], float s) {
-#pragma unroll
-    for (int i = 0; i < E::FM; ++i)
-#pragma unroll
-      for (int j = 0; j < E::FN; ++j)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[i][j][e] *= s;
   }
 };
 
@@ -554,6 +809,16 @@ MUON_INLINE int stage_swz(int r) {
 }
 MUON_INLINE int stage_off(int r, int u) { return r * kOutStride + ((u ^ stage_swz(r)) << 3); }
 
+// threadIdx.x behind an empty asm: address arithmetic derived from it stays
+// where it is written. Without this the compiler hoists the epilogues' per-lane
+// LDS offsets out of the persistent tile loop as loop invariants, keeps dozens
+// of them live across the GEMM, spills them, and reloads them one by one.
+MUON_INLINE int fresh_tid() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
 MUON_INLINE u32x4 bf16x8_bits(v4i16 lo, v4i16 hi) {
   return __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
@@ -571,41 +836,51 @@ MUON_INLINE u32x4 stage_read_row8(const unsigned char* smem, int r, int ch) {
 // r0 .. r0+7 of column c0 + i, where c0 is a multiple of 16 and r0 a multiple
 // of 8 (both uniform over the group). Lane i addresses row r0 + i/4 (and
 // r0 + 4 + i/4), unit c0/4 + i%4.
-MUON_INLINE u32x4 stage_read_col8(const unsigned char* smem, int r0, int c0) {
-  const int i = threadIdx.x & 15;
+MUON_INLINE u32x4 stage_read_col8(const unsigned char* smem, int r0, int c0, int tid) {
+  const int i = tid & 15;
   const int u = (c0 >> 2) + (i & 3);
   const v4i16 lo = lds_read_tr(smem + stage_off(r0 + (i >> 2), u));
   const v4i16 hi = lds_read_tr(smem + stage_off(r0 + 4 + (i >> 2), u));
   return bf16x8_bits(lo, hi);
 }
 
-// bf16 accumulator tile -> staging tile. Lane l's group (i, j, g) holds row
-// wm*WM + 32i + l%32, columns wn*WN + 32j + 8g + 4(l/32) .. +3: one unit.
+// bf16 accumulator tile, times scale, -> staging tile. Lane l's group
+// (i, j, g) holds row wm*WM + 32i + l%32, columns wn*WN + 32j + 8g + 4(l/32)
+// .. +3: one unit. The scale is applied here, where every accumulator is read
+// once anyway, rather than in a pass of its own.
 template <class E>
-MUON_INLINE void acc_to_lds(f32x16 (&acc)[E::FM][E::FN], unsigned char* smem) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+MUON_INLINE void acc_to_lds(f32x16 (&acc)[E::FM][E::FN], unsigned char* smem, float scale) {
+  // Row wr + 32i has stage_swz(lane % 32); unit wu + 8j + 2g, where wu's set
+  // bits and those of 8j + 2g are disjoint, sits at (wu ^ swz) ^ (8j + 2g).
+  const int tid = fresh_tid(), lane = tid & 63, wave = tid >> 6;
   const int wr = E::wave_m(wave) * E::WM + (lane & 31);
   const int wu = E::wave_n(wave) * (E::WN / 4) + (lane >> 5);
+  static_assert(E::WN / 4 >= 8 * E::FN, "unit bits of wu and 8j + 2g must not overlap");
+  unsigned char* row = smem + wr * kOutStride;
+  const int ux = (wu ^ stage_swz(lane & 31)) << 3;
 #pragma unroll
-  for (int i = 0; i < E::FM; ++i)
+  for (int j = 0; j < E::FN; ++j)
 #pragma unroll
-    for (int j = 0; j < E::FN; ++j)
+    for (int g = 0; g < 4; ++g) {
+      unsigned char* p = row + (ux ^ ((8 * j + 2 * g) << 3));
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
+      for (int i = 0; i < E::FM; ++i) {
         u32x2 t;
-        t[0] = pack_bf16x2(acc[i][j][4 * g], acc[i][j][4 * g + 1]);
-        t[1] = pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
-        *reinterpret_cast<u32x2*>(smem + stage_off(wr + 32 * i, wu + 8 * j + 2 * g)) = t;
+        t[0] = pack_bf16x2(scale * acc[i][j][4 * g], scale * acc[i][j][4 * g + 1]);
+        t[1] = pack_bf16x2(scale * acc[i][j][4 * g + 2], scale * acc[i][j][4 * g + 3]);
+        *reinterpret_cast<u32x2*>(p + i * 32 * kOutStride) = t;
       }
+    }
 }
 
 // Zeroes the staging entries at rows >= rl or columns >= cl. Called between
 // two barriers, for edge tiles only.
 template <int NT>
 MUON_INLINE void mask_lds(unsigned char* smem, int rl, int cl) {
+  const int tid = fresh_tid();
 #pragma unroll 1
   for (int p = 0; p < 256 * 64 / NT; ++p) {
-    const int idx = threadIdx.x + p * NT, r = idx >> 6, u = idx & 63;
+    const int idx = tid + p * NT, r = idx >> 6, u = idx & 63;
     const int keep = r < rl ? cl - 4 * u : 0;  // valid columns in this unit
     if (keep >= 4) continue;
     u32x2* q = reinterpret_cast<u32x2*>(smem + stage_off(r, u));
@@ -621,9 +896,10 @@ MUON_INLINE void mask_lds(unsigned char* smem, int rl, int cl) {
 // Staging tile -> the 256 x 256 tile at dst (row stride ld): 32 lanes per row.
 template <int NT>
 MUON_INLINE void lds_to_global(const unsigned char* smem, u16* dst, int64_t ld) {
+  const int tid = fresh_tid();
 #pragma unroll 2
   for (int p = 0; p < 256 * 32 / NT; ++p) {
-    const int idx = threadIdx.x + p * NT, row = idx >> 5, ch = idx & 31;
+    const int idx = tid + p * NT, row = idx >> 5, ch = idx & 31;
     *((g_u32x4*)(dst + row * ld + ch * 8)) = stage_read_row8(smem, row, ch);
   }
 }
@@ -635,23 +911,24 @@ MUON_INLINE void lds_to_global(const unsigned char* smem, u16* dst, int64_t ld) 
 template <int NT>
 MUON_INLINE void lds_to_global_t(const unsigned char* smem, u16* dst_t, int64_t ld_t) {
   constexpr int NW = NT / 64;
-  const int wave = threadIdx.x >> 6, G = (threadIdx.x >> 4) & 3, i = threadIdx.x & 15;
+  const int tid = fresh_tid();
+  const int wave = tid >> 6, G = (tid >> 4) & 3, i = tid & 15;
 #pragma unroll 2
   for (int p = 0; p < 128 / NW; ++p) {
     const int t = wave + p * NW;
     const int c0 = 16 * (t & 15), r0 = 32 * (t >> 4) + 8 * G;
-    *((g_u32x4*)(dst_t + (c0 + i) * ld_t + r0)) = stage_read_col8(smem, r0, c0);
+    *((g_u32x4*)(dst_t + (c0 + i) * ld_t + r0)) = stage_read_col8(smem, r0, c0, tid);
   }
 }
 
-// Writes the accumulator tile, scaled beforehand, to dst and, if dst_t is
-// set, its transpose to dst_t, through one staging pass. Entries outside the
-// first rl rows and cl columns are written as 0. LDS must be free on entry;
-// it is free again on exit.
+// Writes scale times the accumulator tile to dst and, if dst_t is set, its
+// transpose to dst_t, through one staging pass. Entries outside the first rl
+// rows and cl columns are written as 0. LDS must be free on entry; it is free
+// again on exit.
 template <class E>
-MUON_INLINE void store_tile_staged(f32x16 (&acc)[E::FM][E::FN], unsigned char* smem, int rl, int cl,
-                                   u16* dst, int64_t ld, u16* dst_t, int64_t ld_t) {
-  acc_to_lds<E>(acc, smem);
+MUON_INLINE void store_tile_staged(f32x16 (&acc)[E::FM][E::FN], unsigned char* smem, float scale, int rl,
+                                   int cl, u16* dst, int64_t ld, u16* dst_t, int64_t ld_t) {
+  acc_to_lds<E>(acc, smem, scale);
   __syncthreads();
   if (rl < E::BM || cl < E::BN) {
     mask_lds<E::NT>(smem, rl, cl);
@@ -660,6 +937,36 @@ MUON_INLINE void store_tile_staged(f32x16 (&acc)[E::FM][E::FN], unsigned char* s
   lds_to_global<E::NT>(smem, dst, ld);
   if (dst_t) lds_to_global_t<E::NT>(smem, dst_t, ld_t);
   __syncthreads();
+}
+
+// bf16 path: the polynomial is folded so that both diagonal terms have
+// coefficient 1, which the engines add exactly (Engine4 with MFMAs against 0/1
+// fragments). With a' = a (1 if a = 0) and, when b, c != 0, g = c/b:
+//   gram stores    A' = g * A
+//   square stores  B' = B / a' = (b^2 / (c a')) * (A' A' + A')
+//   update forms   X_next = a X + B X = a' * (X + B' X)      (a != 0)
+//                         = B' X                              (a = 0)
+// b = 0 or c = 0 keep g = 1: B' = (c/a') A A, or the elementwise (b/a') A.
+struct Fold {
+  float g;      // gram output scale (times s^2 on the first iteration)
+  float sq;     // square output scale
+  int sq_mode;  // 0: elementwise B' = sq * A; 1: product only; 2: product + diagonal
+  float up;     // update output scale (times s on the first iteration)
+  bool up_diag;
+};
+MUON_INLINE Fold fold_coeffs(const StepCoeffs& co) {
+  Fold f;
+  const float ap = co.a != 0.f ? co.a : 1.f;
+  if (co.b != 0.f && co.c != 0.f) {
+    f.g = co.c / co.b; f.sq = co.b * co.b / co.c / ap; f.sq_mode = 2;
+  } else if (co.c == 0.f) {
+    f.g = 1.f; f.sq = co.b / ap; f.sq_mode = 0;
+  } else {
+    f.g = 1.f; f.sq = co.c / ap; f.sq_mode = 1;
+  }
+  f.up = ap;
+  f.up_diag = co.a != 0.f;
+  return f;
 }
 
 template <class E>
@@ -680,8 +987,8 @@ MUON_INLINE void gram_tile(const PhaseArgs& args, const MatDev& d, int ti, int t
   const int64_t tr = (int64_t)ti * E::BM, tc = (int64_t)tj * E::BN;
   const int m = d.m;
   if constexpr (E::kStageTile) {
-    if (alpha != 1.f) TileWalk<E>::scale(acc, alpha);
-    store_tile_staged<E>(acc, static_cast<unsigned char*>(smem), tile_rows<E>(tr, m), tile_cols<E>(tc, m),
+    alpha *= fold_coeffs(args.co).g;
+    store_tile_staged<E>(acc, static_cast<unsigned char*>(smem), alpha, tile_rows<E>(tr, m), tile_cols<E>(tc, m),
                          A + tr * d.lda + tc, d.lda, mirror ? A + tc * d.lda + tr : nullptr, d.lda);
   } else {
     TileWalk<E>::each(tr, tc, acc, [&](int64_t row0, int64_t col, float v[4]) __attribute__((always_inline)) {
@@ -691,7 +998,7 @@ MUON_INLINE void gram_tile(const PhaseArgs& args, const MatDev& d, int ti, int t
   }
 }
 
-// B = b*A when c = 0: no product, the tile and its mirror are scaled
+// B' = f * A when c = 0: no product, the tile and its mirror are scaled
 // elementwise, 16 bytes per lane.
 template <int NT>
 MUON_INLINE void scale_tile_pair(const u16* A, u16* B, int64_t ld, int64_t tr, int64_t tc, bool mirror,
@@ -721,17 +1028,17 @@ MUON_INLINE void square_tile(const PhaseArgs& args, const MatDev& d, int ti, int
   const int64_t tr = (int64_t)ti * E::BM, tc = (int64_t)tj * E::BN;
   const int m = d.m;
   if constexpr (E::kStageTile) {
-    if (cc == 0.f) {
-      scale_tile_pair<E::NT>(A, B, d.lda, tr, tc, mirror, cb);
+    const Fold f = fold_coeffs(args.co);
+    if (f.sq_mode == 0) {
+      scale_tile_pair<E::NT>(A, B, d.lda, tr, tc, mirror, f.sq);
       return;
     }
-    // B = c * (A*A + (b/c)*A). The engine adds (b/c)*A[i][j] while the K
-    // steps over the tile's columns, which hold A[i][j], are in LDS.
+    // B' = sq * (A' A' + A') (or sq * A' A'). The engine adds A'[i][j] while
+    // the K steps over the tile's columns, which hold it, are in LDS.
     f32x16 acc[E::FM][E::FN];
     E::run(A + tr * d.lda, d.lda, A + tc * d.lda, d.lda, d.mp, static_cast<T*>(smem), acc,
-           tj * (E::BN / E::BK), cb / cc);
-    TileWalk<E>::scale(acc, cc);
-    store_tile_staged<E>(acc, static_cast<unsigned char*>(smem), tile_rows<E>(tr, m), tile_cols<E>(tc, m),
+           f.sq_mode == 2 ? tj * (E::BN / E::BK) : -1, 1.f);
+    store_tile_staged<E>(acc, static_cast<unsigned char*>(smem), f.sq, tile_rows<E>(tr, m), tile_cols<E>(tc, m),
                          B + tr * d.lda + tc, d.lda, mirror ? B + tc * d.lda + tr : nullptr, d.lda);
   } else {
     f32x16 acc[E::FM][E::FN];
@@ -790,21 +1097,22 @@ MUON_INLINE void apply8(const MatDev& d, int64_t gr, int64_t gc, u32x4 ov) {
 template <int NT>
 MUON_INLINE void apply_from_lds(const unsigned char* smem, const MatDev& d, int64_t tr, int64_t tc) {
   const int64_t R = d.rows, C = d.cols;
+  const int tid = fresh_tid();
   if (!d.tall) {
 #pragma unroll 1
     for (int p = 0; p < 256 * 32 / NT; ++p) {
-      const int idx = threadIdx.x + p * NT, row = idx >> 5, ch = idx & 31;
+      const int idx = tid + p * NT, row = idx >> 5, ch = idx & 31;
       const int64_t gr = tr + row, gc = tc + ch * 8;
       if (gr < R && gc < C) apply8(d, gr, gc, stage_read_row8(smem, row, ch));
     }
   } else {
     constexpr int NW = NT / 64;
-    const int wave = threadIdx.x >> 6, G = (threadIdx.x >> 4) & 3, i = threadIdx.x & 15;
+    const int wave = tid >> 6, G = (tid >> 4) & 3, i = tid & 15;
 #pragma unroll 1
     for (int p = 0; p < 128 / NW; ++p) {
       const int t = wave + p * NW;
       const int c0 = 16 * (t & 15), r0 = 32 * (t >> 4) + 8 * G;
-      const u32x4 v = stage_read_col8(smem, r0, c0);  // every lane takes part
+      const u32x4 v = stage_read_col8(smem, r0, c0, tid);  // every lane takes part
       const int64_t gr = tc + c0 + i, gc = tr + r0;
       if (gr < R && gc < C) apply8(d, gr, gc, v);
     }
@@ -820,24 +1128,25 @@ MUON_INLINE void update_tile(const PhaseArgs& args, const MatDev& d, int ti, int
   const T* X = static_cast<const T*>(d.x[src]);
   const int64_t tr = (int64_t)ti * E::BM, tc = (int64_t)tj * E::BN;
   f32x16 acc[E::FM][E::FN];
-  // (B X)[i][j] = sum_k B[i][k] X[k][j]. The bf16 engine also adds a*X[i][j]
-  // while its K steps over this tile's rows are in LDS.
+  // (B X)[i][j] = sum_k B[i][k] X[k][j]. The bf16 engine also adds X[i][j]
+  // while its K steps over this tile's rows are in LDS (B holds B/a there).
+  const Fold f = fold_coeffs(args.co);
   E::run(B + tr * d.lda, d.lda, X + tc, d.ldx, d.mp, static_cast<T*>(smem), acc,
-         E::kStageTile ? ti * (E::BM / E::BK) : -1, args.co.a);
+         E::kStageTile && f.up_diag ? ti * (E::BM / E::BK) : -1, 1.f);
   const float ca = args.co.a;
   // First iteration: X holds the unscaled U, and B was built from s*U, so
   // X1 = s * (a U + B U).
   const float xs = args.first ? args.scale[&d - args.mats] : 1.f;
   const int m = d.m, n = d.n;
   if constexpr (E::kStageTile) {
-    // acc already holds a*X + B*X.
-    if (xs != 1.f) TileWalk<E>::scale(acc, xs);
+    // acc holds X + B' X (or B' X when a = 0).
+    const float us = xs * f.up;
     unsigned char* sm = static_cast<unsigned char*>(smem);
     if constexpr (!LAST) {
-      store_tile_staged<E>(acc, sm, tile_rows<E>(tr, m), tile_cols<E>(tc, n),
+      store_tile_staged<E>(acc, sm, us, tile_rows<E>(tr, m), tile_cols<E>(tc, n),
                            static_cast<T*>(d.x[dst]) + tr * d.ldx + tc, d.ldx, nullptr, 0);
     } else {
-      acc_to_lds<E>(acc, sm);
+      acc_to_lds<E>(acc, sm, us);
       __syncthreads();
       apply_from_lds<E::NT>(sm, d, tr, tc);
       __syncthreads();
@@ -890,7 +1199,7 @@ __global__ void __launch_bounds__(E::NT) phase_kernel(PhaseArgs args) {
     while (true) {
       if (threadIdx.x == 0) s_tile = atomicAdd(args.counter + q, 1);
       __syncthreads();
-      const int t = s_tile;
+      const int t = __builtin_amdgcn_readfirstlane(s_tile);  // uniform: tile state stays scalar
       __syncthreads();  // every thread has read s_tile before thread 0 writes it again
       if (t >= len) break;
       const Tile tile = args.tiles[base + t];
@@ -1091,12 +1400,13 @@ hipError_t launch_phase(int dtype, int variant, Phase ph, const PhaseArgs& args,
   if (dtype != 1) return launch_phase_e<EngineF32<false>, EngineF32<true>>(ph, args, grid, s);
   if (variant == kGemmBK32)
     return launch_phase_e<EngineBF16<2, 4, 32, 4, false>, EngineBF16<2, 4, 32, 4, true>>(ph, args, grid, s);
+  if (variant == kGemm4W) return launch_phase_e<Engine4<false>, Engine4<true>>(ph, args, grid, s);
   return launch_phase_e<EngineBF16<2, 4, 64, 2, false>, EngineBF16<2, 4, 64, 2, true>>(ph, args, grid, s);
 }
 
 int gemm_blocks_per_cu(int dtype, int variant) {
-  // Each bf16 workgroup holds 128 KB of LDS: one per CU. The fp32 engine
-  // uses 66 KB and 256 threads: two per CU.
+  // Each bf16 workgroup (either engine) holds 128 KB of LDS: one per CU. The
+  // fp32 engine uses 66 KB and 256 threads: two per CU.
   (void)variant;
   return dtype == 1 ? 1 : 2;
 }
