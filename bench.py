@@ -57,15 +57,18 @@ def parse():
 
 
 def nsflops(shapes, ns_steps):
-    """Algorithmic flops per step and per kernel kind (same count as the oracle's)."""
-    gram = square = update = 0
+    """Algorithmic flops per step and per kernel kind (same count as the oracle's).
+    "dense" counts full products (4m^2 n + 2m^3 per iteration), the convention
+    of literature that does not exploit the symmetry."""
+    gram = square = update = dense = 0
     for r, c in shapes:
         m, n = min(r, c), max(r, c)
         gram += m * (m + 1) * n
         square += m * m * (m + 1)
         update += 2 * m * m * n
+        dense += 4 * m * m * n + 2 * m ** 3
     return {"gram": gram, "square": square, "update": update,
-            "total": ns_steps * (gram + square + update)}
+            "total": ns_steps * (gram + square + update), "dense": ns_steps * dense}
 
 
 def cpu_baseline(wload, indices):
@@ -168,14 +171,17 @@ def main():
     plan.reset_timing()
     plan.set_timing(True)
 
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # One event before the first step and one after each step: the spans
+    # give per-step times, the first-to-last span the total.
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    start.record(stream)
-    for _ in range(args.steps):
+    ev[0].record(stream)
+    for k in range(args.steps):
         plan.step(stream)
-    end.record(stream)
+        ev[k + 1].record(stream)
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
+    total_ms = ev[0].elapsed_time(ev[-1])
+    step_ms = [ev[k].elapsed_time(ev[k + 1]) for k in range(args.steps)]
     plan.set_timing(False)
     ktimes = plan.kernel_times()
     ms_per_step = total_ms / args.steps
@@ -222,6 +228,9 @@ def main():
                    "beta": wload.beta, "nesterov": wload.nesterov,
                    "alg_tflop_per_step": round(fl["total"] / 1e12, 3)},
         "fraction_of_peak": round(tflops / peak, 4),
+        "step_ms": {"mean": round(ms_per_step, 4), "median": round(float(np.median(step_ms)), 4),
+                    "min": round(min(step_ms), 4), "max": round(max(step_ms), 4)},
+        "dense_equiv_tflops": round(fl["dense"] / (ms_per_step / 1e3) / 1e12, 2),
         "roofline": {
             "kernel": "update (X' = aX + BX; weight apply on the last iteration)",
             "bound": "mfma",
