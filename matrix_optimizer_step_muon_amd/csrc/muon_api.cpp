@@ -294,11 +294,11 @@ muon_status muon_plan(const muon_matrix* mats, int32_t n, const muon_hparams* hp
   int n_cu = 0;
   e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, p->device);
   if (e != hipSuccess) { free_plan(p); return hip_fail(e, "hipDeviceGetAttribute"); }
-  // MUON_GEMM_VARIANT=0|1|2 picks the bf16 engine pipeline (a tuning knob;
+  // MUON_GEMM_VARIANT=0|1|2|3 picks the bf16 engine pipeline (a tuning knob;
   // the default is the four-wave engine, 2).
   if (const char* v = std::getenv("MUON_GEMM_VARIANT")) {
     const int k = std::atoi(v);
-    p->variant = k == 0 ? muon::kGemmBK64 : k == 1 ? muon::kGemmBK32 : muon::kGemm4W;
+    p->variant = k == 0 ? muon::kGemmBK64 : k == 1 ? muon::kGemmBK32 : k == 3 ? muon::kGemm4WDeep : muon::kGemm4W;
   }
   const int32_t resident = n_cu * muon::gemm_blocks_per_cu(p->dtype, p->variant);
   for (int ph = 0; ph < 3; ++ph) p->grid[ph] = std::max(1, std::min(p->n_tiles[ph], resident));

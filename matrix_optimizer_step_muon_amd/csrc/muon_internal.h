@@ -94,8 +94,8 @@ hipError_t launch_norm(const MatDev* mats, const float* partials, float* scale, 
 hipError_t launch_apply(int dtype, const EwArgs& args, int32_t n_blocks, hipStream_t s);
 // bf16 GEMM engine pipelines: 8 waves of 128 x 64 with K step 64 and a ring
 // of 2 LDS stages, or K step 32 and 4 stages; 4 waves of 128 x 128 with K
-// step 64 and 2 stages.
-enum GemmVariant { kGemmBK64 = 0, kGemmBK32 = 1, kGemm4W = 2 };
+// step 64 and 2 stages, or K step 32 and 4 stages.
+enum GemmVariant { kGemmBK64 = 0, kGemmBK32 = 1, kGemm4W = 2, kGemm4WDeep = 3 };
 
 hipError_t launch_phase(int dtype, int variant, Phase ph, const PhaseArgs& args, int32_t grid,
                         hipStream_t s);

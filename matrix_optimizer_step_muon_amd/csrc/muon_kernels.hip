@@ -426,31 +426,60 @@ MUON_INLINE void dma16s(const void* base_, uint32_t voff, uint32_t lds) {
 }
 
 // Four-wave bf16 engine: 2 x 2 waves of 128 x 128 each (accumulators in the
-// AGPR half of the register file), K step 64, a ring of 2 LDS stages.
+// AGPR half of the register file), K step BK, a ring of STAGES LDS stages.
 //
 // With one wave per SIMD nothing else hides a stalled instruction stream, so
 // the loop issues MFMAs one at a time with the rest of the work between
 // them: while MFMA n of a sub-step runs, the wave reads fragment n of the
-// next sub-step (n < 8) and, in sub-step 0, issues DMA instruction n of the
-// next K step. Larger wave tiles read a third less LDS per flop than the
-// eight-wave layout; on a power-capped chip that is worth more than the
-// latency the second wave per SIMD would hide.
+// next sub-step (n < 8) and, in sub-step 0, one of the DMA instructions of
+// the step STAGES - 1 ahead. Larger wave tiles read a third less LDS per flop
+// than the eight-wave layout; on a power-capped chip that is worth more than
+// the latency the second wave per SIMD would hide.
+//
+// The loads are latency-bound, not bandwidth-bound: a CU only streams as many
+// bytes per K step as it keeps in flight. With a ring of 2 stages that is one
+// K step, and steps then last about one memory round trip whatever the MFMA
+// work. K step 32 with 4 stages of 32 KB keeps three steps (96 KB) in flight
+// in the same 128 KB of LDS.
+//
+// Every step issues the loads of one stage, so the vmcnt accounting is the
+// same in every step: waiting for step kt+1 leaves STAGES - 2 later stages in
+// flight. Steps past the end re-load the last K step (L2-hot) into a stage
+// nobody reads; run() drains them before it returns.
 //
 // The operand layouts, the swizzles, the accumulator layout, the diagonal
 // window and the rotated K order are those of EngineBF16.
-template <bool QK>
+template <bool QK, int BK_, int STAGES_>
 struct Engine4 {
   typedef u16 T;
-  static constexpr int BM = 256, BN = 256, BK = 64, STAGES = 2;
+  static constexpr int BM = 256, BN = 256, BK = BK_, STAGES = STAGES_;
   static constexpr int NT = 256, NW = 4;
   static constexpr int WM = 128, WN = 128, FM = 4, FN = 4;
-  static constexpr int S = 8, ROW = 128;             // P rows of 64 bf16
-  static constexpr int OP_BYTES = BM * ROW;          // 32 KB per operand and stage
+  static constexpr int S = BK / 8, ROW = BK * 2;     // P rows: S 16-byte slots
+  static constexpr int RPI = 1024 / ROW;             // P rows per DMA instruction
+  static constexpr int OP_BYTES = BM * ROW;          // per operand and stage
   static constexpr int STAGE_BYTES = 2 * OP_BYTES;
-  static constexpr int DPW = OP_BYTES / 1024 / NW;   // 8 DMA instructions per wave and operand
+  static constexpr int DPW = OP_BYTES / 1024 / NW;   // DMA instructions per wave and operand
+  static constexpr int PS = 2 * DPW;                 // per wave and stage
+  static constexpr int KK = BK / 16;                 // sub-steps per K step
   static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
   static constexpr bool kStageTile = true;
   static constexpr bool kQK = QK;
+  static_assert(DPW % 2 == 0 && 16 % PS == 0 && KK % 2 == 0 && (STAGES & (STAGES - 1)) == 0,
+                "schedule assumptions");
+  // DMA issue slots. A 2-stage ring must have step kt+1's loads issued before
+  // the wait in step kt, so they all go into sub-step 0, one per 16/PS MFMAs.
+  // A deeper ring loads step kt + STAGES - 1 in step kt, needed steps later,
+  // so the loads are spread over the whole step (one per SPREAD MFMAs) and
+  // never queue up behind each other in the CU's DMA path (64 B per clock).
+  static constexpr bool SPREAD_ALL = STAGES >= 3;
+  static constexpr int SPREAD = SPREAD_ALL ? 16 * KK / PS : 16 / PS;
+  static constexpr int WAIT_AT = (KK - 1) * 16 + 8;  // MFMAs of a step issued before its wait
+  static constexpr int DMA_BEFORE_WAIT = SPREAD_ALL ? (WAIT_AT + SPREAD - 1) / SPREAD : PS;
+  // Loads that may still be in flight at the wait for step kt+1: those of
+  // steps kt+2 .. kt+STAGES-2 and the ones of step kt+STAGES-1 already issued.
+  static constexpr int WAIT_N = (STAGES - 3) * PS + DMA_BEFORE_WAIT;
+  static_assert(!SPREAD_ALL || SPREAD * PS == 16 * KK, "spread covers the step");
   static MUON_INLINE int wave_m(int w) { return w >> 1; }
   static MUON_INLINE int wave_n(int w) { return w & 1; }
 
@@ -470,34 +499,35 @@ struct Engine4 {
     const int KT = K / BK;
     const int kt0 = diag_kt0 >= 0 ? diag_kt0 : 0;
     // DMA plan. Instruction p of this wave fills 1 KB of each operand: P rows
-    // 8(wave*DPW + p) .. +7 (lane l: row + l/8, slot l%8, global chunk
-    // slot ^ swz(row) = l%8 ^ l/8 ^ p%2), and Q likewise, or for QK the K rows
-    // 2(wave*DPW + p) .. +1 (lane l: row + l/32, slot l%32, global chunk
-    // slot ^ swzk(row), which depends on p%2 and l/32 only). The per-lane part
-    // of the address depends on p only through p%2: two offsets per operand.
+    // RPI*(wave*DPW + p) .. +RPI-1 (lane l: row + l/S, slot l%S, global chunk
+    // slot ^ swz(row)), Q likewise, or for QK the K rows 2(wave*DPW + p) .. +1
+    // (lane l: row + l/32, slot l%32, global chunk slot ^ swzk(row)). With DPW
+    // even, swz(row) and swzk(row) depend on p only through p%2: the per-lane
+    // part of the address takes two values per operand.
     uint32_t vp[2], vq[2];
 #pragma unroll
     for (int par = 0; par < 2; ++par) {
-      vp[par] = (uint32_t)((lane >> 3) * ldp * 2) + ((((lane & 7) ^ (lane >> 3) ^ par)) << 4);
+      const int prow = (wave * DPW + par) * RPI + lane / S;
+      vp[par] = (uint32_t)((lane / S) * ldp * 2) + (((lane % S) ^ lds_swizzle<S>(prow)) << 4);
       if (QK)
         vq[par] = (uint32_t)((lane >> 5) * ldq * 2) +
-                  (((lane & 31) ^ lds_swizzle_k(2 * par + (lane >> 5))) << 4);
+                  (((lane & 31) ^ lds_swizzle_k(2 * (wave * DPW + par) + (lane >> 5))) << 4);
       else
-        vq[par] = (uint32_t)((lane >> 3) * ldq * 2) + ((((lane & 7) ^ (lane >> 3) ^ par)) << 4);
+        vq[par] = (uint32_t)((lane / S) * ldq * 2) + (((lane % S) ^ lds_swizzle<S>(prow)) << 4);
     }
     const uint32_t lds_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem);
-    // DMA instruction d (0 .. 2*DPW-1) of loop step kt: even d loads P, odd
-    // d loads Q, both for p = d/2.
+    // DMA instruction d (0 .. PS-1) of loop step kt: even d loads P, odd d
+    // loads Q, both for p = d/2. Steps past the end load the last step again.
     auto dma = [&](int kt, int d) __attribute__((always_inline)) {
-      int ks = kt + kt0;
+      int ks = (kt < KT ? kt : KT - 1) + kt0;
       if (ks >= KT) ks -= KT;
       const int p = d >> 1, row = wave * DPW + p;
-      const uint32_t st = lds_base + (kt & 1) * STAGE_BYTES + row * 1024;
+      const uint32_t st = lds_base + (kt & (STAGES - 1)) * STAGE_BYTES + row * 1024;
       if (d & 1) {
-        const u16* qb = QK ? Q + ((int64_t)ks * BK + 2 * row) * ldq : Q + (int64_t)(8 * row) * ldq + ks * BK;
+        const u16* qb = QK ? Q + ((int64_t)ks * BK + 2 * row) * ldq : Q + (int64_t)(RPI * row) * ldq + ks * BK;
         dma16s(qb, vq[p & 1], st + OP_BYTES);
       } else {
-        dma16s(P + (int64_t)(8 * row) * ldp + ks * BK, vp[p & 1], st);
+        dma16s(P + (int64_t)(RPI * row) * ldp + ks * BK, vp[p & 1], st);
       }
     };
 
@@ -519,7 +549,7 @@ struct Engine4 {
     // Read item f (0..3: P block f, 4..7: Q block f-4) of sub-step kk of loop
     // step kt into buffer buf.
     auto rd = [&](int buf, int kt, int kk, int f) __attribute__((always_inline)) {
-      const unsigned char* st = sb + (kt & 1) * STAGE_BYTES;
+      const unsigned char* st = sb + (kt & (STAGES - 1)) * STAGE_BYTES;
       const int fo = (((2 * kk) | h) ^ sw) * 16;
       if (f < FM) {
         fp[buf][f] = *reinterpret_cast<const bf16x8*>(st + rowp + f * 32 * ROW + fo);
@@ -538,18 +568,18 @@ struct Engine4 {
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fq[buf][j], fp[buf][i], acc[i][j], 0, 0, 0);
     };
 
-    // Diagonal window (loop steps 0 .. 3, when diag_kt0 >= 0): the term
-    // added is 1 * (the operand tile at the output tile's own rows or
-    // columns), and it is added by MFMAs against 0/1 selection fragments:
-    // I_t[c][k] = (c == 16t + k) for the 16 K values of a sub-step. Step
-    // slab holds output rows (QK) or columns slab*64 .. +63, owned by the
-    // waves with wm (QK) or wn equal to slab/2, in accumulator blocks
-    // 2*(slab%2) + kk/2. Sub-step kk covers 16 of them, half t = kk%2 of the
-    // block, and the fragments it already holds are the operand values:
+    // Diagonal window (loop steps 0 .. BM/BK - 1, when diag_kt0 >= 0): the
+    // term added is 1 * (the operand tile at the output tile's own rows or
+    // columns), added by MFMAs against 0/1 selection fragments
+    // I_t[c][k] = (c == 16t + k) over the 16 K values of a sub-step. Step s
+    // holds output rows (QK) or columns s*BK .. +BK-1, owned by the waves with
+    // wm (QK) or wn equal to s*BK/128, in accumulator block
+    // (s*BK % 128)/32 + kk/2; sub-step kk covers half t = kk%2 of it. The
+    // fragments the sub-step already holds are the operand values:
     //  - QK (update, X' = X + B X): fq[j] holds X[row][col] with the column
-    //    on lanes, so D += fq[j] * I_t^T adds X to block (2*(slab%2) + kk/2, j);
+    //    on lanes, so D += fq[j] * I_t^T adds X to block (blk, j);
     //  - otherwise (square, A' A' + A'): fp[i] holds P[row][k] with the row
-    //    on lanes, so D += I_t * fp[i] adds A' to block (i, 2*(slab%2) + kk/2).
+    //    on lanes, so D += I_t * fp[i] adds A' to block (i, blk).
     // The diagonal coefficient must be 1 (diag_coef is not used).
     bf16x8 sel[2];
 #pragma unroll
@@ -561,17 +591,15 @@ struct Engine4 {
 
 #define MUON_SB() __builtin_amdgcn_sched_barrier(0)
     // One loop step kt. Fragments of sub-step 0 are in buffer 0 on entry; on
-    // exit those of step kt+1 are. Unless LAST, the step issues the loads of
-    // step kt+1 (K index taken mod KT, so always in bounds) and reads its first
-    // fragments. WIN >= 0: a diagonal-window step whose slab has parity WIN;
-    // the waves that do not own the slab add 0 (their selection fragments are
-    // zero), so every wave runs the same code.
-    auto kstep = [&](int kt, auto LAST_, auto WIN_) __attribute__((always_inline)) {
-      constexpr bool LAST = decltype(LAST_)::value;
+    // exit those of step kt+1 are (after the last step, reads of a stage
+    // nobody uses). WIN >= 0: a diagonal-window step whose first accumulator
+    // block is WIN; the waves that do not own the step's slab add 0 (their
+    // selection fragments are zero), so every wave runs the same code.
+    auto kstep = [&](int kt, auto WIN_) __attribute__((always_inline)) {
       constexpr int WIN = decltype(WIN_)::value;
       bf16x8 ds[2];
       if constexpr (WIN >= 0) {
-        const bool own = (kt >> 1) == (QK ? wm : wn);
+        const bool own = ((kt * BK) >> 7) == (QK ? wm : wn);
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           const u32x4 z = {0u, 0u, 0u, 0u};
@@ -580,7 +608,7 @@ struct Engine4 {
       }
       auto diag = [&](int buf, int kk) __attribute__((always_inline)) {
         if constexpr (WIN >= 0) {
-          const int blk = 2 * WIN + (kk >> 1);
+          const int blk = WIN + (kk >> 1);
 #pragma unroll
           for (int o = 0; o < 4; ++o) {
             if (QK) acc[blk][o] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fq[buf][o], ds[kk & 1], acc[blk][o], 0, 0, 0);
@@ -588,68 +616,79 @@ struct Engine4 {
           }
         }
       };
+      // DMA slot of MFMA g (0 .. 16*KK - 1) of the step.
+      auto dma_slot = [&](int g) __attribute__((always_inline)) {
+        if ((SPREAD_ALL || g < 16) && g % SPREAD == 0) dma(kt + STAGES - 1, g / SPREAD);
+      };
 #pragma unroll
-      for (int kk = 0; kk < 3; ++kk) {
+      for (int kk = 0; kk < KK - 1; ++kk) {
         const int b = kk & 1;
 #pragma unroll
         for (int n = 0; n < 16; ++n) {
           mf(b, n);
           if (n < 8) rd(b ^ 1, kt, kk + 1, n);
-          if (!LAST && kk == 0) dma(kt + 1, n);
+          dma_slot(16 * kk + n);
           MUON_SB();
         }
         diag(b, kk);
         MUON_SB();
       }
-      // Sub-step 3 (buffer 1): half the MFMAs, then wait for this wave's
-      // loads of the next step and the barrier (after it every wave's loads
-      // are in LDS and every wave is done with this step's stage), then the
-      // other half under the first reads of the next step.
+      // Last sub-step (buffer 1): half the MFMAs, then wait for this wave's
+      // loads of step kt+1 and the barrier (after it every wave's loads of
+      // that step are in LDS and every wave is done with this step's stage,
+      // which the next step's DMA overwrites), then the other half under the
+      // first reads of the next step.
 #pragma unroll
-      for (int n = 0; n < 8; ++n) { mf(1, n); MUON_SB(); }
-      if (!LAST) wait_vmcnt<0>();
+      for (int n = 0; n < 8; ++n) {
+        mf(1, n);
+        dma_slot(16 * (KK - 1) + n);
+        MUON_SB();
+      }
+      wait_vmcnt<WAIT_N>();
       __syncthreads();
       MUON_SB();
 #pragma unroll
       for (int n = 8; n < 16; ++n) {
         mf(1, n);
-        if (!LAST) rd(0, kt + 1, 0, n - 8);
+        rd(0, kt + 1, 0, n - 8);
+        dma_slot(16 * (KK - 1) + n);
         MUON_SB();
       }
-      diag(1, 3);  // buffer 1 is intact: the reads above fill buffer 0
+      diag(1, KK - 1);  // buffer 1 is intact: the reads above fill buffer 0
       MUON_SB();
     };
 #undef MUON_SB
-    using F_ = std::false_type;
-    using T_ = std::true_type;
     using NOWIN = std::integral_constant<int, -1>;
-    using W0 = std::integral_constant<int, 0>;
-    using W1 = std::integral_constant<int, 1>;
 
 #pragma unroll
-    for (int d = 0; d < 2 * DPW; ++d) dma(0, d);
-    wait_vmcnt<0>();
+    for (int k = 0; k < STAGES - 1; ++k)
+#pragma unroll
+      for (int d = 0; d < PS; ++d) dma(k, d);
+    wait_vmcnt<(STAGES - 2) * PS>();
     __syncthreads();
 #pragma unroll
     for (int f = 0; f < 8; ++f) rd(0, 0, 0, f);
-    // K >= BM, so KT >= 4 and the window is loop steps 0 .. 3.
+    // K >= BM, so the window's BM/BK steps all exist.
     int kt = 0;
     if (diag_kt0 >= 0) {
-      kstep(0, F_{}, W0{});
-      kstep(1, F_{}, W1{});
-      kstep(2, F_{}, W0{});
-      kstep(3, F_{}, W1{});
-      kt = 4;
+      for (int g = 0; g < BM / 128; ++g) {
+        if constexpr (BK == 64) {
+          kstep(kt, std::integral_constant<int, 0>{});
+          kstep(kt + 1, std::integral_constant<int, 2>{});
+          kt += 2;
+        } else {
+          kstep(kt, std::integral_constant<int, 0>{});
+          kstep(kt + 1, std::integral_constant<int, 1>{});
+          kstep(kt + 2, std::integral_constant<int, 2>{});
+          kstep(kt + 3, std::integral_constant<int, 3>{});
+          kt += 4;
+        }
+      }
     }
-    if (kt < KT) {
-      for (; kt < KT - 1; ++kt) kstep(kt, F_{}, NOWIN{});
-      kstep(KT - 1, T_{}, NOWIN{});
-    } else {
-      // KT == 4 with a window: step 3 loaded a stage nobody reads.
-      wait_vmcnt<0>();
-      __syncthreads();
-    }
-    // The final barrier of the last step leaves the ring free.
+    for (; kt < KT; ++kt) kstep(kt, NOWIN{});
+    // Drain the loads past the end before LDS is reused.
+    wait_vmcnt<0>();
+    __syncthreads();
   }
 };
 
@@ -1400,7 +1439,8 @@ hipError_t launch_phase(int dtype, int variant, Phase ph, const PhaseArgs& args,
   if (dtype != 1) return launch_phase_e<EngineF32<false>, EngineF32<true>>(ph, args, grid, s);
   if (variant == kGemmBK32)
     return launch_phase_e<EngineBF16<2, 4, 32, 4, false>, EngineBF16<2, 4, 32, 4, true>>(ph, args, grid, s);
-  if (variant == kGemm4W) return launch_phase_e<Engine4<false>, Engine4<true>>(ph, args, grid, s);
+  if (variant == kGemm4W) return launch_phase_e<Engine4<false, 64, 2>, Engine4<true, 64, 2>>(ph, args, grid, s);
+  if (variant == kGemm4WDeep) return launch_phase_e<Engine4<false, 32, 4>, Engine4<true, 32, 4>>(ph, args, grid, s);
   return launch_phase_e<EngineBF16<2, 4, 64, 2, false>, EngineBF16<2, 4, 64, 2, true>>(ph, args, grid, s);
 }
 
