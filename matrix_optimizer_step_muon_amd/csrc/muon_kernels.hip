@@ -425,6 +425,67 @@ MUON_INLINE void dma16s(const void* base_, uint32_t voff, uint32_t lds) {
       : "memory");
 }
 
+// threadIdx.x behind an empty asm: address arithmetic derived from it stays
+// where it is written. Without this the compiler hoists per-lane offsets (of
+// the engines' fragment reads and DMA, and of the epilogues) out of the
+// persistent tile loop as loop invariants, keeps dozens of them live across
+// the GEMM, spills them, and reloads them one by one.
+MUON_INLINE int fresh_tid() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
+// Operands of one output tile for Engine4: C = P Q^T over K, or P Q for QK
+// engines, with K steps taken from step kt0 on (mod K/BK). diag: the first
+// BM/BK loop steps form the diagonal window (see Engine4).
+struct Opnd {
+  const u16* P;
+  int64_t ldp;
+  const u16* Q;
+  int64_t ldq;
+  int K;
+  int kt0;
+  int diag;
+};
+
+// A read-only kernel table viewed through the constant address space: the
+// compiler then loads from it with scalar loads, into scalar registers, even
+// after the kernel's own stores (through a generic pointer it has to assume
+// they may alias, and falls back to vector loads that also wait for every
+// store in flight).
+template <class T>
+MUON_INLINE const __attribute__((address_space(4))) T* kconst(const T* p) {
+  return (const __attribute__((address_space(4))) T*)p;
+}
+
+MUON_INLINE Tile load_tile(const Tile* tiles, int i) {
+  const auto& t = kconst(tiles)[i];
+  return Tile{t.mat, t.ij};
+}
+
+MUON_INLINE int64_t uniform64(int64_t v) {
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)v);
+  return (int64_t)(((uint64_t)hi << 32) | (uint64_t)lo);
+}
+
+// The same operands, every field read from the first lane. They are uniform
+// anyway, but the compiler cannot always prove it (for a tile claimed inside
+// the K loop, say), and then it keeps them and all DMA address arithmetic in
+// vector registers.
+MUON_INLINE Opnd uniform(const Opnd& o) {
+  Opnd u;
+  u.P = reinterpret_cast<const u16*>(uniform64((int64_t)(uintptr_t)o.P));
+  u.ldp = uniform64(o.ldp);
+  u.Q = reinterpret_cast<const u16*>(uniform64((int64_t)(uintptr_t)o.Q));
+  u.ldq = uniform64(o.ldq);
+  u.K = __builtin_amdgcn_readfirstlane(o.K);
+  u.kt0 = __builtin_amdgcn_readfirstlane(o.kt0);
+  u.diag = __builtin_amdgcn_readfirstlane(o.diag);
+  return u;
+}
+
 // Four-wave bf16 engine: 2 x 2 waves of 128 x 128 each (accumulators in the
 // AGPR half of the register file), K step BK, a ring of STAGES LDS stages.
 //
@@ -483,11 +544,25 @@ struct Engine4 {
   static MUON_INLINE int wave_m(int w) { return w >> 1; }
   static MUON_INLINE int wave_n(int w) { return w & 1; }
 
-  static MUON_INLINE void run(const u16* __restrict__ P, int64_t ldp, const u16* __restrict__ Q,
-                              int64_t ldq, int K, u16* smem, f32x16 (&acc)[FM][FN],
-                              int diag_kt0 = -1, float diag_coef = 0.f) {
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // Computes tile c into acc. A tile long enough for it claims its successor
+  // while it runs: claim(0), claim(1) and claim(2, n) are called at three
+  // consecutive step boundaries before the last STAGES - 1 steps (claim(2, n)
+  // returns whether there is a successor and then sets n). Those last steps
+  // load n's first STAGES - 1 steps into the ring, so n starts without
+  // waiting for memory; pre: c's own first steps were loaded that way by the
+  // previous call. Without a successor, those steps re-load c's last step into
+  // stages nobody reads, and run() drains them before returning. K is a
+  // multiple of BM, so the step count is a multiple of STAGES and a step past
+  // the end maps to n's step of the same ring stage. Returns whether n was
+  // set. On return every wave is done with the ring's last stage (n's first
+  // steps occupy the others), which the epilogue may use until the next
+  // call's first barrier.
+  template <class Claim>
+  static MUON_INLINE bool run(const Opnd& c, Claim&& claim, Opnd& n, bool pre, u16* smem,
+                              f32x16 (&acc)[FM][FN]) {
+    const int tid = fresh_tid();
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave_m(wave), wn = wave_n(wave);
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -496,38 +571,68 @@ struct Engine4 {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    const int KT = K / BK;
-    const int kt0 = diag_kt0 >= 0 ? diag_kt0 : 0;
+    const int KT = c.K / BK;
+    bool has_next = false;
     // DMA plan. Instruction p of this wave fills 1 KB of each operand: P rows
     // RPI*(wave*DPW + p) .. +RPI-1 (lane l: row + l/S, slot l%S, global chunk
     // slot ^ swz(row)), Q likewise, or for QK the K rows 2(wave*DPW + p) .. +1
     // (lane l: row + l/32, slot l%32, global chunk slot ^ swzk(row)). With DPW
     // even, swz(row) and swzk(row) depend on p only through p%2: the per-lane
-    // part of the address takes two values per operand.
-    uint32_t vp[2], vq[2];
+    // part of the address takes two values per operand (and per tile, since
+    // the row strides differ).
+    auto lane_offsets = [&](int64_t ldp, int64_t ldq, uint32_t (&vp)[2], uint32_t (&vq)[2])
+        __attribute__((always_inline)) {
 #pragma unroll
-    for (int par = 0; par < 2; ++par) {
-      const int prow = (wave * DPW + par) * RPI + lane / S;
-      vp[par] = (uint32_t)((lane / S) * ldp * 2) + (((lane % S) ^ lds_swizzle<S>(prow)) << 4);
-      if (QK)
-        vq[par] = (uint32_t)((lane >> 5) * ldq * 2) +
-                  (((lane & 31) ^ lds_swizzle_k(2 * (wave * DPW + par) + (lane >> 5))) << 4);
-      else
-        vq[par] = (uint32_t)((lane / S) * ldq * 2) + (((lane % S) ^ lds_swizzle<S>(prow)) << 4);
-    }
+      for (int par = 0; par < 2; ++par) {
+        const int prow = (wave * DPW + par) * RPI + lane / S;
+        vp[par] = (uint32_t)((lane / S) * ldp * 2) + (((lane % S) ^ lds_swizzle<S>(prow)) << 4);
+        if (QK)
+          vq[par] = (uint32_t)((lane >> 5) * ldq * 2) +
+                    (((lane & 31) ^ lds_swizzle_k(2 * (wave * DPW + par) + (lane >> 5))) << 4);
+        else
+          vq[par] = (uint32_t)((lane / S) * ldq * 2) + (((lane % S) ^ lds_swizzle<S>(prow)) << 4);
+      }
+    };
+    uint32_t vp[2], vq[2], vpn[2] = {0u, 0u}, vqn[2] = {0u, 0u};
+    lane_offsets(c.ldp, c.ldq, vp, vq);
     const uint32_t lds_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem);
-    // DMA instruction d (0 .. PS-1) of loop step kt: even d loads P, odd d
-    // loads Q, both for p = d/2. Steps past the end load the last step again.
-    auto dma = [&](int kt, int d) __attribute__((always_inline)) {
-      int ks = (kt < KT ? kt : KT - 1) + kt0;
+    // DMA instruction d (0 .. PS-1) of loop step kt of tile c (kt < KT):
+    // even d loads P, odd d loads Q, both for p = d/2.
+    auto dma_cur = [&](int kt, int d) __attribute__((always_inline)) {
+      int ks = kt + c.kt0;
       if (ks >= KT) ks -= KT;
       const int p = d >> 1, row = wave * DPW + p;
       const uint32_t st = lds_base + (kt & (STAGES - 1)) * STAGE_BYTES + row * 1024;
       if (d & 1) {
-        const u16* qb = QK ? Q + ((int64_t)ks * BK + 2 * row) * ldq : Q + (int64_t)(RPI * row) * ldq + ks * BK;
+        const u16* qb = QK ? c.Q + ((int64_t)ks * BK + 2 * row) * c.ldq : c.Q + (int64_t)(RPI * row) * c.ldq + ks * BK;
         dma16s(qb, vq[p & 1], st + OP_BYTES);
       } else {
-        dma16s(P + (int64_t)(RPI * row) * ldp + ks * BK, vp[p & 1], st);
+        dma16s(c.P + (int64_t)(RPI * row) * c.ldp + ks * BK, vp[p & 1], st);
+      }
+    };
+    // The same for any loop step, including those past the end of c.
+    auto dma_any = [&](int kt, int d) __attribute__((always_inline)) {
+      const bool past = kt >= KT, nx = past && has_next;
+      int ks;
+      if (nx) {
+        const int KTn = n.K / BK;
+        ks = kt - KT + n.kt0;
+        if (ks >= KTn) ks -= KTn;
+      } else {
+        ks = (past ? KT - 1 : kt) + c.kt0;
+        if (ks >= KT) ks -= KT;
+      }
+      const int p = d >> 1, row = wave * DPW + p;
+      const uint32_t st = lds_base + (kt & (STAGES - 1)) * STAGE_BYTES + row * 1024;
+      if (d & 1) {
+        const u16* Q = nx ? n.Q : c.Q;
+        const int64_t ldq = nx ? n.ldq : c.ldq;
+        const u16* qb = QK ? Q + ((int64_t)ks * BK + 2 * row) * ldq : Q + (int64_t)(RPI * row) * ldq + ks * BK;
+        dma16s(qb, nx ? vqn[p & 1] : vq[p & 1], st + OP_BYTES);
+      } else {
+        const u16* P = nx ? n.P : c.P;
+        const int64_t ldp = nx ? n.ldp : c.ldp;
+        dma16s(P + (int64_t)(RPI * row) * ldp + ks * BK, nx ? vpn[p & 1] : vp[p & 1], st);
       }
     };
 
@@ -568,7 +673,7 @@ struct Engine4 {
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fq[buf][j], fp[buf][i], acc[i][j], 0, 0, 0);
     };
 
-    // Diagonal window (loop steps 0 .. BM/BK - 1, when diag_kt0 >= 0): the
+    // Diagonal window (loop steps 0 .. BM/BK - 1, when c.diag): the
     // term added is 1 * (the operand tile at the output tile's own rows or
     // columns), added by MFMAs against 0/1 selection fragments
     // I_t[c][k] = (c == 16t + k) over the 16 K values of a sub-step. Step s
@@ -580,14 +685,13 @@ struct Engine4 {
     //    on lanes, so D += fq[j] * I_t^T adds X to block (blk, j);
     //  - otherwise (square, A' A' + A'): fp[i] holds P[row][k] with the row
     //    on lanes, so D += I_t * fp[i] adds A' to block (i, blk).
-    // The diagonal coefficient must be 1 (diag_coef is not used).
+    // The diagonal coefficient is 1.
     bf16x8 sel[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         sel[t][e] = (__bf16)(r32 == 16 * t + 8 * h + e ? 1.f : 0.f);
-    (void)diag_coef;
 
 #define MUON_SB() __builtin_amdgcn_sched_barrier(0)
     // One loop step kt. Fragments of sub-step 0 are in buffer 0 on entry; on
@@ -595,8 +699,11 @@ struct Engine4 {
     // nobody uses). WIN >= 0: a diagonal-window step whose first accumulator
     // block is WIN; the waves that do not own the step's slab add 0 (their
     // selection fragments are zero), so every wave runs the same code.
-    auto kstep = [&](int kt, auto WIN_) __attribute__((always_inline)) {
+    // TAIL: the step may load past the end of c (the last STAGES - 1 steps,
+    // and the window steps, which may be among them).
+    auto kstep = [&](int kt, auto WIN_, auto TAIL_) __attribute__((always_inline)) {
       constexpr int WIN = decltype(WIN_)::value;
+      constexpr bool TAIL = decltype(TAIL_)::value;
       bf16x8 ds[2];
       if constexpr (WIN >= 0) {
         const bool own = ((kt * BK) >> 7) == (QK ? wm : wn);
@@ -618,7 +725,10 @@ struct Engine4 {
       };
       // DMA slot of MFMA g (0 .. 16*KK - 1) of the step.
       auto dma_slot = [&](int g) __attribute__((always_inline)) {
-        if ((SPREAD_ALL || g < 16) && g % SPREAD == 0) dma(kt + STAGES - 1, g / SPREAD);
+        if ((SPREAD_ALL || g < 16) && g % SPREAD == 0) {
+          if constexpr (TAIL) dma_any(kt + STAGES - 1, g / SPREAD);
+          else dma_cur(kt + STAGES - 1, g / SPREAD);
+        }
       };
 #pragma unroll
       for (int kk = 0; kk < KK - 1; ++kk) {
@@ -660,35 +770,62 @@ struct Engine4 {
 #undef MUON_SB
     using NOWIN = std::integral_constant<int, -1>;
 
+    if (pre) {
+      // Step 0 was issued before the previous tile's epilogue, whose stores
+      // came after it: wait for everything (those stores are nearly done).
+      wait_vmcnt<0>();
+    } else {
 #pragma unroll
-    for (int k = 0; k < STAGES - 1; ++k)
+      for (int k = 0; k < STAGES - 1; ++k)
 #pragma unroll
-      for (int d = 0; d < PS; ++d) dma(k, d);
-    wait_vmcnt<(STAGES - 2) * PS>();
+        for (int d = 0; d < PS; ++d) dma_cur(k, d);
+      wait_vmcnt<(STAGES - 2) * PS>();
+    }
     __syncthreads();
 #pragma unroll
     for (int f = 0; f < 8; ++f) rd(0, 0, 0, f);
-    // K >= BM, so the window's BM/BK steps all exist.
+    // K >= BM, so the window's BM/BK steps all exist. A tile claims its
+    // successor only if the claim steps come after the window.
+    using F_ = std::false_type;
+    using T_ = std::true_type;
+    constexpr int WSTEPS = BM / BK;
+    const int CL = KT - (STAGES - 1) - 3;  // first claim step
+    const bool late = CL >= (c.diag ? WSTEPS : 0);
     int kt = 0;
-    if (diag_kt0 >= 0) {
+    auto window = [&](auto TAIL_) __attribute__((always_inline)) {
       for (int g = 0; g < BM / 128; ++g) {
         if constexpr (BK == 64) {
-          kstep(kt, std::integral_constant<int, 0>{});
-          kstep(kt + 1, std::integral_constant<int, 2>{});
+          kstep(kt, std::integral_constant<int, 0>{}, TAIL_);
+          kstep(kt + 1, std::integral_constant<int, 2>{}, TAIL_);
           kt += 2;
         } else {
-          kstep(kt, std::integral_constant<int, 0>{});
-          kstep(kt + 1, std::integral_constant<int, 1>{});
-          kstep(kt + 2, std::integral_constant<int, 2>{});
-          kstep(kt + 3, std::integral_constant<int, 3>{});
+          kstep(kt, std::integral_constant<int, 0>{}, TAIL_);
+          kstep(kt + 1, std::integral_constant<int, 1>{}, TAIL_);
+          kstep(kt + 2, std::integral_constant<int, 2>{}, TAIL_);
+          kstep(kt + 3, std::integral_constant<int, 3>{}, TAIL_);
           kt += 4;
         }
       }
+    };
+    if (late) {
+      if (c.diag) window(F_{});
+      for (; kt < CL; ++kt) kstep(kt, NOWIN{}, F_{});
+      kstep(kt, NOWIN{}, F_{});
+      claim(0, n);
+      kstep(kt + 1, NOWIN{}, F_{});
+      claim(1, n);
+      kstep(kt + 2, NOWIN{}, F_{});
+      has_next = claim(2, n);
+      if (has_next) lane_offsets(n.ldp, n.ldq, vpn, vqn);
+      kt += 3;
+    } else {
+      // Short tile (only the window and a few steps): no successor.
+      if (c.diag) window(T_{});
+      for (; kt < KT - (STAGES - 1); ++kt) kstep(kt, NOWIN{}, F_{});
     }
-    for (; kt < KT; ++kt) kstep(kt, NOWIN{});
-    // Drain the loads past the end before LDS is reused.
-    wait_vmcnt<0>();
-    __syncthreads();
+    for (; kt < KT; ++kt) kstep(kt, NOWIN{}, T_{});
+    if (!has_next) wait_vmcnt<0>();
+    return has_next;
   }
 };
 
@@ -848,15 +985,6 @@ MUON_INLINE int stage_swz(int r) {
 }
 MUON_INLINE int stage_off(int r, int u) { return r * kOutStride + ((u ^ stage_swz(r)) << 3); }
 
-// threadIdx.x behind an empty asm: address arithmetic derived from it stays
-// where it is written. Without this the compiler hoists the epilogues' per-lane
-// LDS offsets out of the persistent tile loop as loop invariants, keeps dozens
-// of them live across the GEMM, spills them, and reloads them one by one.
-MUON_INLINE int fresh_tid() {
-  int t = threadIdx.x;
-  asm volatile("" : "+v"(t));
-  return t;
-}
 
 MUON_INLINE u32x4 bf16x8_bits(v4i16 lo, v4i16 hi) {
   return __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -1252,6 +1380,341 @@ __global__ void __launch_bounds__(E::NT) phase_kernel(PhaseArgs args) {
   }
 }
 
+// ------------------------------------------------------------ four-wave persistent kernel
+//
+// The four-wave engine pipelines across tiles: while a tile's last K steps
+// run, the ring already receives the next tile's first steps, so a tile starts
+// without waiting for memory. The epilogue therefore only has the LDS those
+// steps leave free: the ring's last stage and the 32 KB after the ring, 64 KB
+// in all, which hold one half of the output tile (128 rows of the staging
+// layout) at a time. Each half is written from the accumulators of the two
+// waves that hold it, then read back by all four waves: by rows for the tile
+// itself (16 bytes per lane, whole 512-byte rows per wave instruction), by
+// columns with ds_read_b64_tr_b16 for the transposed copies.
+
+constexpr int kEpiRows = 128;
+constexpr int kEpiBytes = kEpiRows * kOutStride;  // 64 KB
+constexpr int kEpiExtra = 32 * 1024;              // LDS past the ring
+
+// Half H: scale * tile rows 128H .. 128H+127 into the staging rows of epi.
+// They are the accumulators of the waves with wm = H; the other waves write
+// nothing. Entries outside the matrix are masked when the half is read out.
+template <class E, int H>
+MUON_INLINE void stage_half(f32x16 (&acc)[E::FM][E::FN], unsigned char* epi, float scale) {
+  static_assert(E::WM == kEpiRows, "a staged half is one row of waves");
+  static_assert(E::WN / 4 >= 8 * E::FN, "unit bits of wu and 8j + 2g must not overlap");
+  const int tid = fresh_tid(), lane = tid & 63, wave = tid >> 6;
+  if (E::wave_m(wave) != H) return;
+  const int wu = E::wave_n(wave) * (E::WN / 4) + (lane >> 5);
+  const int ux = (wu ^ stage_swz(lane & 31)) << 3;
+#pragma unroll
+  for (int i = 0; i < E::FM; ++i) {
+    unsigned char* row = epi + (32 * i + (lane & 31)) * kOutStride;
+#pragma unroll
+    for (int j = 0; j < E::FN; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        u32x2 t;
+        t[0] = pack_bf16x2(scale * acc[i][j][4 * g], scale * acc[i][j][4 * g + 1]);
+        t[1] = pack_bf16x2(scale * acc[i][j][4 * g + 2], scale * acc[i][j][4 * g + 3]);
+        *reinterpret_cast<u32x2*>(row + (ux ^ ((8 * j + 2 * g) << 3))) = t;
+      }
+  }
+}
+
+// Eight bf16 of one run (element e in half e%2 of word e/2) with the
+// elements at positions p0 + e >= lim zeroed, all of them unless ok.
+MUON_INLINE u32x4 mask_run(u32x4 v, bool ok, int p0, int lim) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t m = (p0 + 2 * e < lim ? 0xffffu : 0u) | (p0 + 2 * e + 1 < lim ? 0xffff0000u : 0u);
+    v[e] &= ok ? m : 0u;
+  }
+  return v;
+}
+
+// Staged half H -> dst rows 128H .. +127 (dst: the tile's first element, row
+// stride ld, 16-byte aligned rows), entries at tile rows >= rl or columns >= cl
+// as zero. The padding of the operand buffers stays zero that way.
+template <int NT>
+MUON_INLINE void rows_out(const unsigned char* epi, u16* dst, int64_t ld, int H, int rl, int cl) {
+  const int tid = fresh_tid();
+  if (rl >= 256 && cl >= 256) {
+#pragma unroll 4
+    for (int p = 0; p < kEpiRows * 32 / NT; ++p) {
+      const int idx = tid + p * NT, row = idx >> 5, ch = idx & 31;
+      *((g_u32x4*)(dst + (int64_t)(kEpiRows * H + row) * ld + 8 * ch)) = stage_read_row8(epi, row, ch);
+    }
+  } else {
+#pragma unroll 4
+    for (int p = 0; p < kEpiRows * 32 / NT; ++p) {
+      const int idx = tid + p * NT, row = idx >> 5, ch = idx & 31;
+      const u32x4 v = mask_run(stage_read_row8(epi, row, ch), kEpiRows * H + row < rl, 8 * ch, cl);
+      *((g_u32x4*)(dst + (int64_t)(kEpiRows * H + row) * ld + 8 * ch)) = v;
+    }
+  }
+}
+
+// Staged half H -> the transpose: row c of dst_t (c = 0 .. 255) gets columns
+// 128H .. +127 from column c of the staged rows (masked as in rows_out). Wave
+// task t: columns 16(t%16) .. +15, rows 32(t/16) .. +31, lane group G taking 8
+// of those rows, so one wave instruction writes 64 contiguous bytes of each of
+// 16 rows.
+template <int NT>
+MUON_INLINE void mirror_out(const unsigned char* epi, u16* dst_t, int64_t ld_t, int H, int rl, int cl) {
+  constexpr int NW = NT / 64;
+  const int tid = fresh_tid();
+  const int wave = tid >> 6, G = (tid >> 4) & 3, i = tid & 15;
+  const bool edge = rl < 256 || cl < 256;
+#pragma unroll 4
+  for (int p = 0; p < 64 / NW; ++p) {
+    const int t = wave + p * NW;
+    const int c0 = 16 * (t & 15), r0 = 32 * (t >> 4) + 8 * G;
+    u32x4 v = stage_read_col8(epi, r0, c0, tid);
+    if (edge) v = mask_run(v, c0 + i < cl, kEpiRows * H + r0, rl);
+    *((g_u32x4*)(dst_t + (int64_t)(c0 + i) * ld_t + kEpiRows * H + r0)) = v;
+  }
+}
+
+// Last iteration, staged half H of the X tile (rows tr + 128H .., columns tc
+// ..). Wide matrix: W rows tr + 128H + r, read by rows; tall matrix (X = the
+// transposed update): W columns tr + 128H .. of W rows tc + c, read by
+// columns. A thread's 16 runs of 8 are applied in one batch: all W loads are
+// in flight together, so the half costs one memory round trip, not 16.
+// What the last iteration's apply needs of a matrix, as scalars.
+struct ApplyDev {
+  u16* w;
+  u16* delta;
+  float ls;
+  int64_t rows, cols;
+  int tall;
+};
+
+template <int NT>
+MUON_INLINE void apply_half(const unsigned char* epi, const ApplyDev& d, int64_t tr, int64_t tc, int H) {
+  constexpr int N = kEpiRows * 32 / NT;
+  constexpr int NW = NT / 64;
+  static_assert(N == 64 / NW, "row and column item counts agree");
+  const int64_t R = d.rows, C = d.cols;
+  u16* W = d.w;
+  u16* D = d.delta;
+  const float ls = d.ls;
+  const int tid = fresh_tid();
+  const int wave = tid >> 6, G = (tid >> 4) & 3, i = tid & 15;
+  u32x4 ov[N], wv[N];
+  int64_t gr[N], gc[N];
+#pragma unroll
+  for (int p = 0; p < N; ++p) {
+    if (!d.tall) {
+      const int idx = tid + p * NT, row = idx >> 5, ch = idx & 31;
+      gr[p] = tr + kEpiRows * H + row;
+      gc[p] = tc + ch * 8;
+      ov[p] = stage_read_row8(epi, row, ch);
+    } else {
+      const int t = wave + p * NW;
+      const int c0 = 16 * (t & 15), r0 = 32 * (t >> 4) + 8 * G;
+      gr[p] = tc + c0 + i;
+      gc[p] = tr + kEpiRows * H + r0;
+      ov[p] = stage_read_col8(epi, r0, c0, tid);  // every lane takes part
+    }
+  }
+  // Whole aligned runs: W loaded for all items first.
+#pragma unroll
+  for (int p = 0; p < N; ++p) {
+    const int64_t base = gr[p] * C + gc[p];
+    const bool fast = gr[p] < R && gc[p] + 8 <= C && (base & 7) == 0;
+    wv[p] = u32x4{0u, 0u, 0u, 0u};
+    if (W && fast) wv[p] = *((const g_u32x4*)(W + base));
+  }
+#pragma unroll
+  for (int p = 0; p < N; ++p) {
+    if (gr[p] >= R || gc[p] >= C) continue;
+    const int64_t base = gr[p] * C + gc[p];
+    if (gc[p] + 8 <= C && (base & 7) == 0) {
+      float o[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o[2 * e] = __uint_as_float(ov[p][e] << 16);
+        o[2 * e + 1] = __uint_as_float(ov[p][e] & 0xffff0000u);
+      }
+      if (W) {
+        u32x4 nv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          nv[e] = pack_bf16x2(__uint_as_float(wv[p][e] << 16) - ls * o[2 * e],
+                              __uint_as_float(wv[p][e] & 0xffff0000u) - ls * o[2 * e + 1]);
+        *((g_u32x4*)(W + base)) = nv;
+      }
+      if (D) {
+        u32x4 dv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dv[e] = pack_bf16x2(-ls * o[2 * e], -ls * o[2 * e + 1]);
+        *((g_u32x4*)(D + base)) = dv;
+      }
+    } else {  // ragged edge or unaligned row: element by element
+      for (int e = 0; e < 8 && gc[p] + e < C; ++e) {
+        const float o = __uint_as_float(e & 1 ? ov[p][e >> 1] & 0xffff0000u : ov[p][e >> 1] << 16);
+        if (W) Elem<u16>::store(W + base + e, Elem<u16>::load(W + base + e) - ls * o);
+        if (D) Elem<u16>::store(D + base + e, -ls * o);
+      }
+    }
+  }
+}
+
+template <class E, int PH>
+__global__ void __launch_bounds__(E::NT) phase_kernel4(PhaseArgs args) {
+  static_assert(E::LDS_BYTES + kEpiExtra <= 160 * 1024, "ring + staging exceed LDS");
+  static_assert(E::STAGE_BYTES >= kEpiBytes - kEpiExtra, "the staging half must not reach the preloaded stages");
+  __shared__ __attribute__((aligned(16))) unsigned char smem[E::LDS_BYTES + kEpiExtra];
+  unsigned char* epi = smem + E::LDS_BYTES + kEpiExtra - kEpiBytes;
+  // Tile claims go through one word past the ring: free while a tile runs
+  // (the epilogue is the only other user of that LDS).
+  int* s_tile = reinterpret_cast<int*>(smem + E::LDS_BYTES);
+  const Fold f = fold_coeffs(args.co);
+  const int home = blockIdx.x % kQueues;
+  int qq = 0;  // queues home + 0 .. qq-1 are known to be empty
+  // Next tile of this workgroup (index into args.tiles), or -1: its home
+  // queue first, then the others. Every thread calls it (it has barriers).
+  auto fetch = [&]() -> int {
+    while (qq < kQueues) {
+      const int q = __builtin_amdgcn_readfirstlane((home + qq) % kQueues);
+      if (threadIdx.x == 0) *s_tile = atomicAdd(args.counter + q, 1);
+      __syncthreads();
+      const int t = __builtin_amdgcn_readfirstlane(*s_tile);
+      __syncthreads();  // every thread has read s_tile before it is written again
+      const int base = kconst(args.qoff)[q];
+      if (t < kconst(args.qoff)[q + 1] - base) return base + t;
+      ++qq;
+    }
+    return -1;
+  };
+  if constexpr (PH == kSquare) {
+    if (f.sq_mode == 0) {  // B' = sq * A elementwise: no product
+      for (int t = fetch(); t >= 0; t = fetch()) {
+        const Tile tile = args.tiles[t];
+        const MatDev& d = args.mats[tile.mat];
+        const int64_t tr = (int64_t)(tile.ij >> 16) * E::BM, tc = (int64_t)(tile.ij & 0xffff) * E::BN;
+        scale_tile_pair<E::NT>(static_cast<const u16*>(d.a), static_cast<u16*>(d.b), d.lda, tr, tc,
+                               (tile.ij >> 16) != (tile.ij & 0xffff), f.sq);
+      }
+      return;
+    }
+  }
+  auto operands = [&](int t) __attribute__((always_inline)) {
+    const Tile tile = load_tile(args.tiles, __builtin_amdgcn_readfirstlane(t));
+    const auto& d = kconst(args.mats)[tile.mat];
+    const int ti = tile.ij >> 16, tj = tile.ij & 0xffff;
+    const int64_t tr = (int64_t)ti * E::BM, tc = (int64_t)tj * E::BN;
+    Opnd o;
+    if constexpr (PH == kGram) {
+      const u16* X = static_cast<const u16*>(d.x[args.src]);
+      o = Opnd{X + tr * d.ldx, d.ldx, X + tc * d.ldx, d.ldx, d.np, 0, 0};
+    } else if constexpr (PH == kSquare) {
+      const u16* A = static_cast<const u16*>(d.a);
+      const int dg = f.sq_mode == 2;
+      o = Opnd{A + tr * d.lda, d.lda, A + tc * d.lda, d.lda, d.mp, dg ? tj * (E::BN / E::BK) : 0, dg};
+    } else {
+      const u16* B = static_cast<const u16*>(d.b);
+      const u16* X = static_cast<const u16*>(d.x[args.src]);
+      o = Opnd{B + tr * d.lda, d.lda, X + tc, d.ldx, d.mp, ti * (E::BM / E::BK), 1};
+      if (!f.up_diag) { o.kt0 = 0; o.diag = 0; }
+    }
+    return uniform(o);
+  };
+  // In-loop claim of the successor from the current queue (see Engine4::run):
+  // thread 0 takes a ticket, parks it in s_tile after a step's barrier has
+  // passed, and every thread reads it after the next step's barrier. An empty
+  // queue moves qq on and leaves the successor to fetch().
+  int ticket = 0, nxt = -1;
+  auto claim = [&](int st, Opnd& n) __attribute__((always_inline)) -> bool {
+    if (qq >= kQueues) return false;
+    const int q = __builtin_amdgcn_readfirstlane((home + qq) % kQueues);
+    if (st == 0) {
+      if (threadIdx.x == 0) ticket = atomicAdd(args.counter + q, 1);
+      return false;
+    }
+    if (st == 1) {
+      if (threadIdx.x == 0) *s_tile = ticket;
+      return false;
+    }
+    const int t = __builtin_amdgcn_readfirstlane(*s_tile);
+    const int base = kconst(args.qoff)[q];
+    if (t >= kconst(args.qoff)[q + 1] - base) {
+      ++qq;
+      return false;
+    }
+    nxt = __builtin_amdgcn_readfirstlane(base + t);
+    n = operands(nxt);
+    return true;
+  };
+  int cur = fetch();
+  if (cur < 0) return;
+  Opnd oc = operands(cur);
+  bool pre = false;
+  while (true) {
+    f32x16 acc[E::FM][E::FN];
+    Opnd on;
+    nxt = -1;
+    const bool has_next = E::run(oc, claim, on, pre, reinterpret_cast<u16*>(smem), acc);
+
+    const Tile tile = load_tile(args.tiles, __builtin_amdgcn_readfirstlane(cur));
+    const auto& d = kconst(args.mats)[tile.mat];
+    const int ti = tile.ij >> 16, tj = tile.ij & 0xffff;
+    const int64_t tr = (int64_t)ti * E::BM, tc = (int64_t)tj * E::BN;
+    const float s = kconst(args.scale)[tile.mat];
+    // Each half: stage, barrier, read out, barrier (the second half's closing
+    // barrier is the next tile's first one when it was preloaded).
+    if constexpr (PH == kGram || PH == kSquare) {
+      // gram: A' = g s^2 U U^T on the first iteration (X holds U), else g X X^T.
+      // square: B' = sq * (A' A' + A').
+      const float sc = PH == kGram ? (args.first ? s * s : 1.f) * f.g : f.sq;
+      u16* O = static_cast<u16*>(PH == kGram ? d.a : d.b);
+      const int rl = tile_rows<E>(tr, d.m), cl = tile_cols<E>(tc, d.m);
+      auto half = [&](auto H_) __attribute__((always_inline)) {
+        constexpr int H = decltype(H_)::value;
+        stage_half<E, H>(acc, epi, sc);
+        __syncthreads();
+        rows_out<E::NT>(epi, O + tr * d.lda + tc, d.lda, H, rl, cl);
+        if (ti != tj) mirror_out<E::NT>(epi, O + tc * d.lda + tr, d.lda, H, rl, cl);
+      };
+      half(std::integral_constant<int, 0>{});
+      __syncthreads();
+      half(std::integral_constant<int, 1>{});
+    } else {
+      // X_next = s' * a' * (X + B' X), s' = s on the first iteration.
+      const float us = (args.first ? s : 1.f) * f.up;
+      auto half = [&](auto H_) __attribute__((always_inline)) {
+        constexpr int H = decltype(H_)::value;
+        if constexpr (PH == kUpdate) {
+          stage_half<E, H>(acc, epi, us);
+          __syncthreads();
+          rows_out<E::NT>(epi, static_cast<u16*>(d.x[args.src ^ 1]) + tr * d.ldx + tc, d.ldx, H,
+                          tile_rows<E>(tr, d.m), tile_cols<E>(tc, d.n));
+        } else {
+          stage_half<E, H>(acc, epi, us);
+          __syncthreads();
+          const ApplyDev ad{static_cast<u16*>(d.w), static_cast<u16*>(d.delta), d.lr_scale, d.rows, d.cols, d.tall};
+          apply_half<E::NT>(epi, ad, tr, tc, H);
+        }
+      };
+      half(std::integral_constant<int, 0>{});
+      __syncthreads();
+      half(std::integral_constant<int, 1>{});
+    }
+    if (has_next) {
+      cur = nxt;
+      oc = on;
+      pre = true;
+    } else {
+      __syncthreads();  // the staging half is read out before fetch() writes s_tile
+      cur = fetch();
+      if (cur < 0) break;
+      oc = operands(cur);
+      pre = false;
+    }
+  }
+}
+
 // ------------------------------------------------------------ elementwise kernels
 
 // Matrix of elementwise block b: the last i with prefix[i] <= b.
@@ -1434,13 +1897,27 @@ static hipError_t launch_phase_e(Phase ph, const PhaseArgs& args, int32_t grid, 
   return hipGetLastError();
 }
 
+// The four-wave engine's kernels (tile pipelining, epilogues off the ring).
+template <class E, class EQ>
+static hipError_t launch_phase_e4(Phase ph, const PhaseArgs& args, int32_t grid, hipStream_t s) {
+  switch (ph) {
+    case kGram: hipLaunchKernelGGL((phase_kernel4<E, kGram>), dim3(grid), dim3(E::NT), 0, s, args); break;
+    case kSquare: hipLaunchKernelGGL((phase_kernel4<E, kSquare>), dim3(grid), dim3(E::NT), 0, s, args); break;
+    default:
+      if (args.last) hipLaunchKernelGGL((phase_kernel4<EQ, kUpdateLast>), dim3(grid), dim3(EQ::NT), 0, s, args);
+      else hipLaunchKernelGGL((phase_kernel4<EQ, kUpdate>), dim3(grid), dim3(EQ::NT), 0, s, args);
+      break;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_phase(int dtype, int variant, Phase ph, const PhaseArgs& args, int32_t grid,
                         hipStream_t s) {
   if (dtype != 1) return launch_phase_e<EngineF32<false>, EngineF32<true>>(ph, args, grid, s);
   if (variant == kGemmBK32)
     return launch_phase_e<EngineBF16<2, 4, 32, 4, false>, EngineBF16<2, 4, 32, 4, true>>(ph, args, grid, s);
-  if (variant == kGemm4W) return launch_phase_e<Engine4<false, 64, 2>, Engine4<true, 64, 2>>(ph, args, grid, s);
-  if (variant == kGemm4WDeep) return launch_phase_e<Engine4<false, 32, 4>, Engine4<true, 32, 4>>(ph, args, grid, s);
+  if (variant == kGemm4W) return launch_phase_e4<Engine4<false, 64, 2>, Engine4<true, 64, 2>>(ph, args, grid, s);
+  if (variant == kGemm4WDeep) return launch_phase_e4<Engine4<false, 32, 4>, Engine4<true, 32, 4>>(ph, args, grid, s);
   return launch_phase_e<EngineBF16<2, 4, 64, 2, false>, EngineBF16<2, 4, 64, 2, true>>(ph, args, grid, s);
 }
 
