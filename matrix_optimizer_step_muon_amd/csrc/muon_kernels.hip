@@ -1396,20 +1396,24 @@ constexpr int kEpiRows = 128;
 constexpr int kEpiBytes = kEpiRows * kOutStride;  // 64 KB
 constexpr int kEpiExtra = 32 * 1024;              // LDS past the ring
 
-// Half H: scale * tile rows 128H .. 128H+127 into the staging rows of epi.
-// They are the accumulators of the waves with wm = H; the other waves write
-// nothing. Entries outside the matrix are masked when the half is read out.
+// Half H of the output tile: accumulator blocks 2H and 2H+1 of every wave,
+// i.e. tile rows 64H .. +63 and 128 + 64H .. +63, times scale, into the 128
+// staging rows of epi (staged row r holds tile row half_row(r, H)). All four
+// waves convert in both halves. Entries outside the matrix are masked when the
+// half is read out.
+MUON_INLINE int half_row(int r, int H) { return (r & 63) + ((r >> 6) << 7) + 64 * H; }
+
 template <class E, int H>
 MUON_INLINE void stage_half(f32x16 (&acc)[E::FM][E::FN], unsigned char* epi, float scale) {
-  static_assert(E::WM == kEpiRows, "a staged half is one row of waves");
+  static_assert(E::WM == 128 && E::FM == 4 && E::BM == 256, "halves are blocks {0,1} and {2,3} of 128-row waves");
   static_assert(E::WN / 4 >= 8 * E::FN, "unit bits of wu and 8j + 2g must not overlap");
   const int tid = fresh_tid(), lane = tid & 63, wave = tid >> 6;
-  if (E::wave_m(wave) != H) return;
   const int wu = E::wave_n(wave) * (E::WN / 4) + (lane >> 5);
   const int ux = (wu ^ stage_swz(lane & 31)) << 3;
 #pragma unroll
-  for (int i = 0; i < E::FM; ++i) {
-    unsigned char* row = epi + (32 * i + (lane & 31)) * kOutStride;
+  for (int ii = 0; ii < 2; ++ii) {
+    const int i = 2 * H + ii;
+    unsigned char* row = epi + (64 * E::wave_m(wave) + 32 * ii + (lane & 31)) * kOutStride;
 #pragma unroll
     for (int j = 0; j < E::FN; ++j)
 #pragma unroll
@@ -1433,7 +1437,7 @@ MUON_INLINE u32x4 mask_run(u32x4 v, bool ok, int p0, int lim) {
   return v;
 }
 
-// Staged half H -> dst rows 128H .. +127 (dst: the tile's first element, row
+// Staged half H -> its 128 rows of dst (dst: the tile's first element, row
 // stride ld, 16-byte aligned rows), entries at tile rows >= rl or columns >= cl
 // as zero. The padding of the operand buffers stays zero that way.
 template <int NT>
@@ -1443,20 +1447,21 @@ MUON_INLINE void rows_out(const unsigned char* epi, u16* dst, int64_t ld, int H,
 #pragma unroll 4
     for (int p = 0; p < kEpiRows * 32 / NT; ++p) {
       const int idx = tid + p * NT, row = idx >> 5, ch = idx & 31;
-      *((g_u32x4*)(dst + (int64_t)(kEpiRows * H + row) * ld + 8 * ch)) = stage_read_row8(epi, row, ch);
+      *((g_u32x4*)(dst + (int64_t)half_row(row, H) * ld + 8 * ch)) = stage_read_row8(epi, row, ch);
     }
   } else {
 #pragma unroll 4
     for (int p = 0; p < kEpiRows * 32 / NT; ++p) {
       const int idx = tid + p * NT, row = idx >> 5, ch = idx & 31;
-      const u32x4 v = mask_run(stage_read_row8(epi, row, ch), kEpiRows * H + row < rl, 8 * ch, cl);
-      *((g_u32x4*)(dst + (int64_t)(kEpiRows * H + row) * ld + 8 * ch)) = v;
+      const int tr = half_row(row, H);
+      const u32x4 v = mask_run(stage_read_row8(epi, row, ch), tr < rl, 8 * ch, cl);
+      *((g_u32x4*)(dst + (int64_t)tr * ld + 8 * ch)) = v;
     }
   }
 }
 
-// Staged half H -> the transpose: row c of dst_t (c = 0 .. 255) gets columns
-// 128H .. +127 from column c of the staged rows (masked as in rows_out). Wave
+// Staged half H -> the transpose: row c of dst_t (c = 0 .. 255) gets, at the
+// half's 128 tile rows, column c of the staged rows (masked as in rows_out). Wave
 // task t: columns 16(t%16) .. +15, rows 32(t/16) .. +31, lane group G taking 8
 // of those rows, so one wave instruction writes 64 contiguous bytes of each of
 // 16 rows.
@@ -1470,16 +1475,16 @@ MUON_INLINE void mirror_out(const unsigned char* epi, u16* dst_t, int64_t ld_t, 
   for (int p = 0; p < 64 / NW; ++p) {
     const int t = wave + p * NW;
     const int c0 = 16 * (t & 15), r0 = 32 * (t >> 4) + 8 * G;
+    const int tr0 = half_row(r0, H);  // 8 staged rows, 8 consecutive tile rows
     u32x4 v = stage_read_col8(epi, r0, c0, tid);
-    if (edge) v = mask_run(v, c0 + i < cl, kEpiRows * H + r0, rl);
-    *((g_u32x4*)(dst_t + (int64_t)(c0 + i) * ld_t + kEpiRows * H + r0)) = v;
+    if (edge) v = mask_run(v, c0 + i < cl, tr0, rl);
+    *((g_u32x4*)(dst_t + (int64_t)(c0 + i) * ld_t + tr0)) = v;
   }
 }
 
-// Last iteration, staged half H of the X tile (rows tr + 128H .., columns tc
-// ..). Wide matrix: W rows tr + 128H + r, read by rows; tall matrix (X = the
-// transposed update): W columns tr + 128H .. of W rows tc + c, read by
-// columns. A thread's 16 runs of 8 are applied in one batch: all W loads are
+// Last iteration, staged half H of the X tile (tile rows half_row(r, H)).
+// Wide matrix: W rows tr + half_row(r, H), read by rows; tall matrix (X = the
+// transposed update): those W columns of W rows tc + c, read by columns. A thread's 16 runs of 8 are applied in one batch: all W loads are
 // in flight together, so the half costs one memory round trip, not 16.
 // What the last iteration's apply needs of a matrix, as scalars.
 struct ApplyDev {
@@ -1507,14 +1512,14 @@ MUON_INLINE void apply_half(const unsigned char* epi, const ApplyDev& d, int64_t
   for (int p = 0; p < N; ++p) {
     if (!d.tall) {
       const int idx = tid + p * NT, row = idx >> 5, ch = idx & 31;
-      gr[p] = tr + kEpiRows * H + row;
+      gr[p] = tr + half_row(row, H);
       gc[p] = tc + ch * 8;
       ov[p] = stage_read_row8(epi, row, ch);
     } else {
       const int t = wave + p * NW;
       const int c0 = 16 * (t & 15), r0 = 32 * (t >> 4) + 8 * G;
       gr[p] = tc + c0 + i;
-      gc[p] = tr + kEpiRows * H + r0;
+      gc[p] = tr + half_row(r0, H);
       ov[p] = stage_read_col8(epi, r0, c0, tid);  // every lane takes part
     }
   }
