@@ -63,10 +63,21 @@ struct muon_plan_s {
   float* d_scale = nullptr;
   int32_t* d_counters = nullptr;
   int32_t n_counters = 0;
-  muon::Tile* d_tiles[3] = {nullptr, nullptr, nullptr};
-  int32_t* d_qoff = nullptr;  // 3 x (kQueues + 1) queue offsets
-  int32_t n_tiles[3] = {0, 0, 0};
-  int32_t grid[3] = {0, 0, 0};
+  // GEMM phases run as `chains` independent chains of launches over disjoint
+  // groups of matrices, chain 0 on the caller's stream and chain c on aux[c-1].
+  // A chain's persistent kernel takes CUs only as the other chain's kernel
+  // retires workgroups, i.e. in its tail, so the chains fill each other's
+  // tails. Per chain: one tile table per phase.
+  struct Chain {
+    muon::Tile* d_tiles[3] = {nullptr, nullptr, nullptr};
+    int32_t* d_qoff = nullptr;  // 3 x (kQueues + 1) queue offsets
+    int32_t n_tiles[3] = {0, 0, 0};
+    int32_t grid[3] = {0, 0, 0};
+  };
+  std::vector<Chain> chains;
+  std::vector<hipStream_t> aux;
+  hipEvent_t ev_fork = nullptr;
+  std::vector<hipEvent_t> ev_join;
   int32_t ew_blocks = 0;
 
   bool timing = false;
@@ -149,6 +160,9 @@ muon_status validate(const muon_matrix* mats, int32_t n, const muon_hparams* hp)
 
 void free_plan(muon_plan_s* p) {
   if (!p) return;
+  for (auto st : p->aux) (void)hipStreamDestroy(st);
+  for (auto e : p->ev_join) (void)hipEventDestroy(e);
+  if (p->ev_fork) (void)hipEventDestroy(p->ev_fork);
   if (p->ws) (void)hipFree(p->ws);
   for (auto& r : p->pending) { (void)hipEventDestroy(r.start); (void)hipEventDestroy(r.end); }
   for (auto e : p->pool) (void)hipEventDestroy(e);
@@ -220,7 +234,39 @@ muon_status muon_plan(const muon_matrix* mats, int32_t n, const muon_hparams* hp
   const size_t o_prefix = take(sizeof(int32_t) * (n + 1));
   const size_t o_parts = take(sizeof(float) * std::max(parts, 1));
   const size_t o_scale = take(sizeof(float) * n);
-  p->n_counters = std::max(3 * hp->ns_steps * muon::kQueues, 1);
+  // MUON_GEMM_VARIANT=0|1|2|3 picks the bf16 engine pipeline (a tuning knob;
+  // the default is the four-wave engine, 2).
+  if (const char* v = std::getenv("MUON_GEMM_VARIANT")) {
+    const int k = std::atoi(v);
+    p->variant = k == 0 ? muon::kGemmBK64 : k == 1 ? muon::kGemmBK32 : k == 3 ? muon::kGemm4WDeep : muon::kGemm4W;
+  }
+  // Chains: two for the bf16 four-wave engines (MUON_CHAINS=C overrides, C in
+  // [1, 8]), one otherwise; never more than there are matrices. Matrices go
+  // largest first (multiply-adds of one iteration) to the lightest chain.
+  int C = (p->dtype == 1 && (p->variant == muon::kGemm4W || p->variant == muon::kGemm4WDeep)) ? 2 : 1;
+  if (const char* v = std::getenv("MUON_CHAINS")) C = std::max(1, std::min(8, std::atoi(v)));
+  C = std::min<int>(C, n);
+  std::vector<std::vector<int32_t>> members(C);
+  {
+    std::vector<std::pair<int64_t, int32_t>> wts(n);
+    for (int32_t i = 0; i < n; ++i) {
+      const muon::MatDev& d = p->mats[i];
+      const int64_t tm = d.mp / T, tn = d.np / T, sym = tm * (tm + 1) / 2;
+      wts[i] = {sym * d.np + sym * d.mp + tm * tn * d.mp, i};
+    }
+    std::stable_sort(wts.begin(), wts.end(), [](const auto& x, const auto& y) { return x.first > y.first; });
+    std::vector<int64_t> load(C, 0);
+    for (const auto& w : wts) {
+      int best = 0;
+      for (int c = 1; c < C; ++c)
+        if (load[c] < load[best]) best = c;
+      load[best] += w.first;
+      members[best].push_back(w.second);
+    }
+    for (auto& g : members) std::sort(g.begin(), g.end());
+  }
+  p->chains.resize(C);
+  p->n_counters = std::max(C * 3 * hp->ns_steps * muon::kQueues, 1);
   const size_t o_ctr = take(sizeof(int32_t) * p->n_counters);
 
   // Tile tables. Each phase's tiles are cut into blocks of kBlockRows x
@@ -230,7 +276,7 @@ muon_status muon_plan(const muon_matrix* mats, int32_t n, const muon_hparams* hp
   // the same area, so the cost is tiles x K. Ties keep (matrix, block) order,
   // and a block's tiles stay in row-major order.
   struct Block { int64_t cost; std::vector<muon::Tile> tiles; };
-  std::vector<Block> blocks[3];
+  std::vector<Block> blocks[8][3];
   // Blocks are walked column-major: consecutive blocks, dealt to different
   // XCDs, share the column operand's panels in the Infinity Cache. Tuning
   // knobs: MUON_BLOCK=RxC sets the block shape in tiles, and
@@ -241,7 +287,8 @@ muon_status muon_plan(const muon_matrix* mats, int32_t n, const muon_hparams* hp
     if (std::sscanf(v, "%dx%d", &r, &c) == 2 && r > 0 && c > 0 && r * c <= 1024) { brows = r; bcols = c; }
   }
   if (const char* v = std::getenv("MUON_BLOCK_ORDER")) border = std::atoi(v) != 0;
-  for (int32_t i = 0; i < n; ++i) {
+  for (int c = 0; c < C; ++c)
+  for (int32_t i : members[c]) {
     const muon::MatDev& d = p->mats[i];
     const int32_t tm = int32_t(d.mp / T), tn = int32_t(d.np / T);
     for (int ph = 0; ph < 3; ++ph) {
@@ -257,34 +304,38 @@ muon_status muon_plan(const muon_matrix* mats, int32_t n, const muon_hparams* hp
             if (ph == muon::kUpdate || c >= a) b.tiles.push_back({i, (a << 16) | c});
         if (b.tiles.empty()) continue;
         b.cost = int64_t(b.tiles.size()) * K;
-        blocks[ph].push_back(std::move(b));
+        blocks[c][ph].push_back(std::move(b));
       }
     }
   }
-  size_t o_tiles[3];
-  const size_t o_qoff = take(sizeof(int32_t) * 3 * (muon::kQueues + 1));
-  std::vector<muon::Tile> tiles[3];
-  std::vector<int32_t> qoff(3 * (muon::kQueues + 1), 0);
+  size_t o_tiles[8][3];
+  size_t o_qoff[8];
+  std::vector<muon::Tile> tiles[8][3];
+  std::vector<int32_t> qoff[8];
+  for (int c = 0; c < C; ++c) {
+  o_qoff[c] = take(sizeof(int32_t) * 3 * (muon::kQueues + 1));
+  qoff[c].assign(3 * (muon::kQueues + 1), 0);
   for (int ph = 0; ph < 3; ++ph) {
-    std::stable_sort(blocks[ph].begin(), blocks[ph].end(),
+    std::stable_sort(blocks[c][ph].begin(), blocks[c][ph].end(),
                      [](const Block& x, const Block& y) { return x.cost > y.cost; });
     std::vector<std::vector<muon::Tile>> q(muon::kQueues);
     int64_t load[muon::kQueues] = {};
-    for (const Block& b : blocks[ph]) {
+    for (const Block& b : blocks[c][ph]) {
       int best = 0;
       for (int k = 1; k < muon::kQueues; ++k)
         if (load[k] < load[best]) best = k;
       load[best] += b.cost;
       q[best].insert(q[best].end(), b.tiles.begin(), b.tiles.end());
     }
-    int32_t* qo = &qoff[ph * (muon::kQueues + 1)];
+    int32_t* qo = &qoff[c][ph * (muon::kQueues + 1)];
     for (int k = 0; k < muon::kQueues; ++k) {
-      qo[k] = int32_t(tiles[ph].size());
-      tiles[ph].insert(tiles[ph].end(), q[k].begin(), q[k].end());
+      qo[k] = int32_t(tiles[c][ph].size());
+      tiles[c][ph].insert(tiles[c][ph].end(), q[k].begin(), q[k].end());
     }
-    qo[muon::kQueues] = int32_t(tiles[ph].size());
-    p->n_tiles[ph] = int32_t(tiles[ph].size());
-    o_tiles[ph] = take(sizeof(muon::Tile) * std::max<size_t>(tiles[ph].size(), 1));
+    qo[muon::kQueues] = int32_t(tiles[c][ph].size());
+    p->chains[c].n_tiles[ph] = int32_t(tiles[c][ph].size());
+    o_tiles[c][ph] = take(sizeof(muon::Tile) * std::max<size_t>(tiles[c][ph].size(), 1));
+  }
   }
   p->ws_bytes = cursor;
 
@@ -294,14 +345,25 @@ muon_status muon_plan(const muon_matrix* mats, int32_t n, const muon_hparams* hp
   int n_cu = 0;
   e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, p->device);
   if (e != hipSuccess) { free_plan(p); return hip_fail(e, "hipDeviceGetAttribute"); }
-  // MUON_GEMM_VARIANT=0|1|2|3 picks the bf16 engine pipeline (a tuning knob;
-  // the default is the four-wave engine, 2).
-  if (const char* v = std::getenv("MUON_GEMM_VARIANT")) {
-    const int k = std::atoi(v);
-    p->variant = k == 0 ? muon::kGemmBK64 : k == 1 ? muon::kGemmBK32 : k == 3 ? muon::kGemm4WDeep : muon::kGemm4W;
-  }
   const int32_t resident = n_cu * muon::gemm_blocks_per_cu(p->dtype, p->variant);
-  for (int ph = 0; ph < 3; ++ph) p->grid[ph] = std::max(1, std::min(p->n_tiles[ph], resident));
+  for (auto& ch : p->chains)
+    for (int ph = 0; ph < 3; ++ph) ch.grid[ph] = std::max(1, std::min(ch.n_tiles[ph], resident));
+  // Auxiliary streams (default priority, not synchronising with the null
+  // stream) and the fork / join events of the chains.
+  for (int c = 1; c < C; ++c) {
+    hipStream_t st = nullptr;
+    e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking);
+    if (e != hipSuccess) { free_plan(p); return hip_fail(e, "hipStreamCreateWithFlags"); }
+    p->aux.push_back(st);
+    hipEvent_t ev = nullptr;
+    e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+    if (e != hipSuccess) { free_plan(p); return hip_fail(e, "hipEventCreateWithFlags"); }
+    p->ev_join.push_back(ev);
+  }
+  if (C > 1) {
+    e = hipEventCreateWithFlags(&p->ev_fork, hipEventDisableTiming);
+    if (e != hipSuccess) { free_plan(p); return hip_fail(e, "hipEventCreateWithFlags"); }
+  }
 
   e = hipMalloc(&p->ws, p->ws_bytes);
   if (e != hipSuccess) {
@@ -325,18 +387,20 @@ muon_status muon_plan(const muon_matrix* mats, int32_t n, const muon_hparams* hp
   p->d_partials = reinterpret_cast<float*>(base + o_parts);
   p->d_scale = reinterpret_cast<float*>(base + o_scale);
   p->d_counters = reinterpret_cast<int32_t*>(base + o_ctr);
-  for (int ph = 0; ph < 3; ++ph) p->d_tiles[ph] = reinterpret_cast<muon::Tile*>(base + o_tiles[ph]);
-  p->d_qoff = reinterpret_cast<int32_t*>(base + o_qoff);
-
   struct Up { void* dst; const void* src; size_t bytes; };
-  const Up ups[6] = {
+  std::vector<Up> ups = {
       {p->d_mats, p->mats.data(), sizeof(muon::MatDev) * n},
-      {p->d_qoff, qoff.data(), sizeof(int32_t) * qoff.size()},
       {p->d_prefix, prefix.data(), sizeof(int32_t) * (n + 1)},
-      {p->d_tiles[0], tiles[0].data(), sizeof(muon::Tile) * tiles[0].size()},
-      {p->d_tiles[1], tiles[1].data(), sizeof(muon::Tile) * tiles[1].size()},
-      {p->d_tiles[2], tiles[2].data(), sizeof(muon::Tile) * tiles[2].size()},
   };
+  for (int c = 0; c < C; ++c) {
+    muon_plan_s::Chain& ch = p->chains[c];
+    ch.d_qoff = reinterpret_cast<int32_t*>(base + o_qoff[c]);
+    ups.push_back({ch.d_qoff, qoff[c].data(), sizeof(int32_t) * qoff[c].size()});
+    for (int ph = 0; ph < 3; ++ph) {
+      ch.d_tiles[ph] = reinterpret_cast<muon::Tile*>(base + o_tiles[c][ph]);
+      ups.push_back({ch.d_tiles[ph], tiles[c][ph].data(), sizeof(muon::Tile) * tiles[c][ph].size()});
+    }
+  }
   for (const Up& u : ups) {
     if (u.bytes == 0) continue;
     e = hipMemcpy(u.dst, u.src, u.bytes, hipMemcpyHostToDevice);
@@ -360,7 +424,12 @@ muon_status muon_plan_info(muon_plan_t p, int64_t* n_tiles, int64_t* grid) {
     int64_t t = 0, g = 0;
     if (k == MUON_K_MOMENTUM || k == MUON_K_APPLY) { t = p->ew_blocks; g = p->ew_blocks; }
     else if (k == MUON_K_NORM) { t = p->n; g = p->n; }
-    else { t = p->n_tiles[k - MUON_K_GRAM]; g = p->grid[k - MUON_K_GRAM]; }
+    else {
+      for (const auto& ch : p->chains) {
+        t += ch.n_tiles[k - MUON_K_GRAM];
+        g = std::max<int64_t>(g, ch.grid[k - MUON_K_GRAM]);
+      }
+    }
     if (n_tiles) n_tiles[k] = t;
     if (grid) grid[k] = g;
   }
@@ -417,22 +486,26 @@ muon_status muon_step(muon_plan_t p, void* stream) {
     return hipEventCreate(out);
   };
   muon_status st = MUON_OK;
-  auto run = [&](int kind, auto&& launch) {
+  auto run_on = [&](hipStream_t q, int kind, auto&& launch) {
     if (st != MUON_OK) return;
     hipEvent_t a = nullptr, b = nullptr;
     if (p->timing) {
       hipError_t r = ev(&a);
       if (r == hipSuccess) r = ev(&b);
-      if (r == hipSuccess) r = hipEventRecord(a, s);
+      if (r == hipSuccess) r = hipEventRecord(a, q);
       if (r != hipSuccess) { st = hip_fail(r, "timing event"); return; }
     }
     hipError_t r = launch();
     if (r != hipSuccess) { st = hip_fail(r, "kernel launch"); return; }
     if (p->timing) {
-      r = hipEventRecord(b, s);
+      r = hipEventRecord(b, q);
       if (r != hipSuccess) { st = hip_fail(r, "hipEventRecord"); return; }
       p->pending.push_back({kind, a, b});
     }
+  };
+  auto run = [&](int kind, auto&& launch) { run_on(s, kind, launch); };
+  auto sync = [&](hipError_t r, const char* what) {
+    if (st == MUON_OK && r != hipSuccess) st = hip_fail(r, what);
   };
 
   muon::StepCoeffs co{p->hp.a, p->hp.b, p->hp.c, p->hp.beta, p->hp.eps, p->hp.nesterov};
@@ -443,13 +516,29 @@ muon_status muon_step(muon_plan_t p, void* stream) {
   if (T == 0) {
     run(MUON_K_APPLY, [&] { return muon::launch_apply(p->dtype, ew, p->ew_blocks, s); });
   }
+  const int C = int(p->chains.size());
+  if (T > 0 && C > 1) {
+    sync(hipEventRecord(p->ev_fork, s), "hipEventRecord");
+    for (auto q : p->aux) sync(hipStreamWaitEvent(q, p->ev_fork, 0), "hipStreamWaitEvent");
+  }
   for (int it = 0; it < T; ++it) {
     for (int ph = 0; ph < 3; ++ph) {
-      muon::PhaseArgs a{p->d_mats, p->d_tiles[ph], p->d_qoff + ph * (muon::kQueues + 1),
-                        p->d_counters + (3 * it + ph) * muon::kQueues, p->d_scale, it & 1, it == 0,
-                        it == T - 1, co};
-      run(MUON_K_GRAM + ph,
-          [&] { return muon::launch_phase(p->dtype, p->variant, muon::Phase(ph), a, p->grid[ph], s); });
+      for (int c = 0; c < C; ++c) {
+        const muon_plan_s::Chain& ch = p->chains[c];
+        if (ch.n_tiles[ph] == 0) continue;
+        hipStream_t q = c == 0 ? s : p->aux[c - 1];
+        muon::PhaseArgs a{p->d_mats, ch.d_tiles[ph], ch.d_qoff + ph * (muon::kQueues + 1),
+                          p->d_counters + ((c * T + it) * 3 + ph) * muon::kQueues, p->d_scale, it & 1, it == 0,
+                          it == T - 1, co};
+        run_on(q, MUON_K_GRAM + ph,
+               [&] { return muon::launch_phase(p->dtype, p->variant, muon::Phase(ph), a, ch.grid[ph], q); });
+      }
+    }
+  }
+  if (T > 0 && C > 1) {
+    for (int c = 1; c < C; ++c) {
+      sync(hipEventRecord(p->ev_join[c - 1], p->aux[c - 1]), "hipEventRecord");
+      sync(hipStreamWaitEvent(s, p->ev_join[c - 1], 0), "hipStreamWaitEvent");
     }
   }
   if (cur != p->device) (void)hipSetDevice(cur);
