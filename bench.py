@@ -50,6 +50,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", default="1,2,0,3",
                     help="matrix indices the oracle times for the CPU baseline")
+    ap.add_argument("--chains", type=int, default=0,
+                    help="GEMM chains of the plan (sets MUON_CHAINS; 0: the library default)")
+    ap.add_argument("--no-roofline-pass", action="store_true",
+                    help="skip the separate single-chain pass that times the update kernel alone")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain elementwise copy kernel (torch.add, fp32) over this "
                          "many MiB, the reference for scaling HBM byte counters")
@@ -160,6 +164,8 @@ def main():
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
+    if args.chains > 0:
+        os.environ["MUON_CHAINS"] = str(args.chains)
     plan = mu.Plan(dev, **wload.hparams())
     info = plan.info()
     print(f"[bench] plan: workspace {plan.workspace_bytes() / 2**30:.2f} GiB, {info}",
@@ -196,12 +202,46 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    # The update kernel's roofline. With two chains the update launches of
+    # one chain share the GPU with the other chain's kernels in their tails,
+    # so their durations do not measure the kernel; it is timed alone, in a
+    # separate pass over the same inputs with one chain.
+    upd_times = ktimes["update"]
+    upd_chains = None
+    if ktimes["update"][1] and ktimes["update"][1] // args.steps > wload.ns_steps and not args.no_roofline_pass:
+        saved = os.environ.get("MUON_CHAINS")
+        os.environ["MUON_CHAINS"] = "1"
+        try:
+            plan1 = mu.Plan(dev, **wload.hparams())
+        finally:
+            if saved is None:
+                del os.environ["MUON_CHAINS"]
+            else:
+                os.environ["MUON_CHAINS"] = saved
+        for _ in range(args.warmup):
+            plan1.step(stream)
+        torch.cuda.synchronize()
+        plan1.reset_timing()
+        plan1.set_timing(True)
+        for _ in range(args.steps):
+            plan1.step(stream)
+        torch.cuda.synchronize()
+        plan1.set_timing(False)
+        upd_times = plan1.kernel_times()["update"]
+        upd_chains = 1
+        plan1.close()
+        print(f"[bench] roofline pass: {args.steps} single-chain steps", file=sys.stderr, flush=True)
+
     fl = nsflops(wload.shapes, wload.ns_steps)
     tflops = fl["total"] / (ms_per_step / 1e3) / 1e12
     peak = BF16_PEAK_TFLOPS if wload.dtype == "bf16" else F32_PEAK_TFLOPS
-    upd_ms, upd_n = ktimes["update"]
+    # Update launches: ns_steps per chain and step, each over its chain's
+    # matrices. Flops per launch = the step's update flops / its launches.
+    upd_ms, upd_n = upd_times
     upd_avg = upd_ms / max(upd_n, 1)
-    upd_tflops = fl["update"] / (upd_avg / 1e3) / 1e12 if upd_n else None
+    upd_per_step = upd_n / args.steps if upd_n else 0
+    upd_flops = fl["update"] * wload.ns_steps / upd_per_step if upd_n else 0.0
+    upd_tflops = upd_flops / (upd_avg / 1e3) / 1e12 if upd_n else None
     per_kernel = {k: {"avg_ms": round(v[0] / v[1], 4), "launches": v[1],
                       "ms_per_step": round(v[0] / args.steps, 4)} for k, v in ktimes.items() if v[1]}
     elem = 2 if wload.dtype == "bf16" else 4
@@ -240,7 +280,10 @@ def main():
             "frac": round(upd_tflops / peak, 4) if upd_tflops else None,
             "traffic": committed_traffic(args.workload),
             "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-scaled)",
-            "alg_tflop_per_launch": round(fl["update"] / 1e12, 4),
+            "alg_tflop_per_launch": round(upd_flops / 1e12, 4),
+            "launches_per_step": upd_per_step,
+            "timed_in": ("a separate single-chain pass of the same steps" if upd_chains == 1
+                         else "the timed region"),
             "avg_launch_ms": round(upd_avg, 4),
         },
         "kernels": per_kernel,
