@@ -599,8 +599,11 @@ struct Engine4 {
     // DMA instruction d (0 .. PS-1) of loop step kt of tile c (kt < KT):
     // even d loads P, odd d loads Q, both for p = d/2.
     auto dma_cur = [&](int kt, int d) __attribute__((always_inline)) {
-      int ks = kt + c.kt0;
-      if (ks >= KT) ks -= KT;
+      int ks = kt;
+      if constexpr (!QK) {  // QK tiles run K in order (no window to put first)
+        ks += c.kt0;
+        if (ks >= KT) ks -= KT;
+      }
       const int p = d >> 1, row = wave * DPW + p;
       const uint32_t st = lds_base + (kt & (STAGES - 1)) * STAGE_BYTES + row * 1024;
       if (d & 1) {
@@ -616,11 +619,17 @@ struct Engine4 {
       int ks;
       if (nx) {
         const int KTn = n.K / BK;
-        ks = kt - KT + n.kt0;
-        if (ks >= KTn) ks -= KTn;
+        ks = kt - KT;
+        if constexpr (!QK) {
+          ks += n.kt0;
+          if (ks >= KTn) ks -= KTn;
+        }
       } else {
-        ks = (past ? KT - 1 : kt) + c.kt0;
-        if (ks >= KT) ks -= KT;
+        ks = past ? KT - 1 : kt;
+        if constexpr (!QK) {
+          ks += c.kt0;
+          if (ks >= KT) ks -= KT;
+        }
       }
       const int p = d >> 1, row = wave * DPW + p;
       const uint32_t st = lds_base + (kt & (STAGES - 1)) * STAGE_BYTES + row * 1024;
@@ -790,9 +799,11 @@ struct Engine4 {
     using T_ = std::true_type;
     constexpr int WSTEPS = BM / BK;
     const int CL = KT - (STAGES - 1) - 3;  // first claim step
-    const bool late = CL >= (c.diag ? WSTEPS : 0);
+    const bool win = !QK && c.diag;        // QK tiles (the update) have no diagonal window
+    const bool late = CL >= (win ? WSTEPS : 0);
     int kt = 0;
     auto window = [&](auto TAIL_) __attribute__((always_inline)) {
+      if constexpr (QK) return;
       for (int g = 0; g < BM / 128; ++g) {
         if constexpr (BK == 64) {
           kstep(kt, std::integral_constant<int, 0>{}, TAIL_);
@@ -808,7 +819,7 @@ struct Engine4 {
       }
     };
     if (late) {
-      if (c.diag) window(F_{});
+      if (win) window(F_{});
       for (; kt < CL; ++kt) kstep(kt, NOWIN{}, F_{});
       kstep(kt, NOWIN{}, F_{});
       claim(0, n);
@@ -820,7 +831,7 @@ struct Engine4 {
       kt += 3;
     } else {
       // Short tile (only the window and a few steps): no successor.
-      if (c.diag) window(T_{});
+      if (win) window(T_{});
       for (; kt < KT - (STAGES - 1); ++kt) kstep(kt, NOWIN{}, F_{});
     }
     for (; kt < KT; ++kt) kstep(kt, NOWIN{}, T_{});
@@ -1114,6 +1125,12 @@ MUON_INLINE void store_tile_staged(f32x16 (&acc)[E::FM][E::FN], unsigned char* s
 //   update forms   X_next = a X + B X = a' * (X + B' X)      (a != 0)
 //                         = B' X                              (a = 0)
 // b = 0 or c = 0 keep g = 1: B' = (c/a') A A, or the elementwise (b/a') A.
+// The four-wave kernels fold the update's identity term into the square's
+// output instead: it stores B'' = B' + I (a != 0), with the 1 added in fp32
+// before the one rounding to bf16, and the update forms a' * B'' X. Late in
+// the iteration X X^T is close to I and B' close to -0.8 I, so rounding
+// 1 + B'_ii once loses less than rounding B'_ii and adding 1 exactly; and the
+// update tiles need no diagonal window, so all of them run K in one order.
 struct Fold {
   float g;      // gram output scale (times s^2 on the first iteration)
   float sq;     // square output scale
@@ -1166,20 +1183,23 @@ MUON_INLINE void gram_tile(const PhaseArgs& args, const MatDev& d, int ti, int t
 }
 
 // B' = f * A when c = 0: no product, the tile and its mirror are scaled
-// elementwise, 16 bytes per lane.
+// elementwise, 16 bytes per lane. On a diagonal tile, 1 is added to the first
+// diag_rows diagonal entries (0: none).
 template <int NT>
 MUON_INLINE void scale_tile_pair(const u16* A, u16* B, int64_t ld, int64_t tr, int64_t tc, bool mirror,
-                                 float cb) {
+                                 float cb, int diag_rows = 0) {
 #pragma unroll 1
   for (int p = 0; p < 256 * 32 / NT; ++p) {
     const int idx = threadIdx.x + p * NT, row = idx >> 5, ch = idx & 31;
+    const int dcol = row < diag_rows ? row - 8 * ch : -1;  // the diagonal entry's place in the run
 #pragma unroll 1
     for (int s = 0; s < (mirror ? 2 : 1); ++s) {
       const int64_t o = (s ? (tc + row) * ld + tr : (tr + row) * ld + tc) + ch * 8;
       u32x4 v = *((const g_u32x4*)(A + o));
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        v[e] = pack_bf16x2(cb * __uint_as_float(v[e] << 16), cb * __uint_as_float(v[e] & 0xffff0000u));
+        v[e] = pack_bf16x2(cb * __uint_as_float(v[e] << 16) + (dcol == 2 * e ? 1.f : 0.f),
+                           cb * __uint_as_float(v[e] & 0xffff0000u) + (dcol == 2 * e + 1 ? 1.f : 0.f));
       *((g_u32x4*)(B + o)) = v;
     }
   }
@@ -1403,13 +1423,20 @@ constexpr int kEpiExtra = 32 * 1024;              // LDS past the ring
 // half is read out.
 MUON_INLINE int half_row(int r, int H) { return (r & 63) + ((r >> 6) << 7) + 64 * H; }
 
-template <class E, int H>
+// EYE: add 1 on the tile's diagonal after scaling (a diagonal tile). Element
+// (R, C) of a wave tile is lane l's register 4g + q of block (i, j), with
+// R = 32i + l%32 and C = 32j + 8g + 4(l/32) + q: on the diagonal iff the wave
+// sits on the tile's diagonal (wm = wn), i = j and l%32 = 8g + 4(l/32) + q.
+template <class E, int H, bool EYE = false>
 MUON_INLINE void stage_half(f32x16 (&acc)[E::FM][E::FN], unsigned char* epi, float scale) {
   static_assert(E::WM == 128 && E::FM == 4 && E::BM == 256, "halves are blocks {0,1} and {2,3} of 128-row waves");
   static_assert(E::WN / 4 >= 8 * E::FN, "unit bits of wu and 8j + 2g must not overlap");
   const int tid = fresh_tid(), lane = tid & 63, wave = tid >> 6;
   const int wu = E::wave_n(wave) * (E::WN / 4) + (lane >> 5);
   const int ux = (wu ^ stage_swz(lane & 31)) << 3;
+  const int l = lane & 31;
+  const bool eye = EYE && E::wave_m(wave) == E::wave_n(wave) && ((l >> 2) & 1) == (lane >> 5);
+  const int er = 4 * (l >> 3) + (l & 3);  // the register holding the diagonal element
 #pragma unroll
   for (int ii = 0; ii < 2; ++ii) {
     const int i = 2 * H + ii;
@@ -1418,9 +1445,15 @@ MUON_INLINE void stage_half(f32x16 (&acc)[E::FM][E::FN], unsigned char* epi, flo
     for (int j = 0; j < E::FN; ++j)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
+        float v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          v[q] = scale * acc[i][j][4 * g + q];
+          if (EYE && i == j) v[q] += (eye && 4 * g + q == er) ? 1.f : 0.f;
+        }
         u32x2 t;
-        t[0] = pack_bf16x2(scale * acc[i][j][4 * g], scale * acc[i][j][4 * g + 1]);
-        t[1] = pack_bf16x2(scale * acc[i][j][4 * g + 2], scale * acc[i][j][4 * g + 3]);
+        t[0] = pack_bf16x2(v[0], v[1]);
+        t[1] = pack_bf16x2(v[2], v[3]);
         *reinterpret_cast<u32x2*>(row + (ux ^ ((8 * j + 2 * g) << 3))) = t;
       }
   }
@@ -1599,8 +1632,9 @@ __global__ void __launch_bounds__(E::NT) phase_kernel4(PhaseArgs args) {
         const Tile tile = args.tiles[t];
         const MatDev& d = args.mats[tile.mat];
         const int64_t tr = (int64_t)(tile.ij >> 16) * E::BM, tc = (int64_t)(tile.ij & 0xffff) * E::BN;
-        scale_tile_pair<E::NT>(static_cast<const u16*>(d.a), static_cast<u16*>(d.b), d.lda, tr, tc,
-                               (tile.ij >> 16) != (tile.ij & 0xffff), f.sq);
+        const bool dt = (tile.ij >> 16) == (tile.ij & 0xffff);
+        scale_tile_pair<E::NT>(static_cast<const u16*>(d.a), static_cast<u16*>(d.b), d.lda, tr, tc, !dt, f.sq,
+                               f.up_diag && dt ? tile_rows<E>(tr, d.m) : 0);
       }
       return;
     }
@@ -1621,8 +1655,7 @@ __global__ void __launch_bounds__(E::NT) phase_kernel4(PhaseArgs args) {
     } else {
       const u16* B = static_cast<const u16*>(d.b);
       const u16* X = static_cast<const u16*>(d.x[args.src]);
-      o = Opnd{B + tr * d.lda, d.lda, X + tc, d.ldx, d.mp, ti * (E::BM / E::BK), 1};
-      if (!f.up_diag) { o.kt0 = 0; o.diag = 0; }
+      o = Opnd{B + tr * d.lda, d.lda, X + tc, d.ldx, d.mp, 0, 0};  // B'' holds the identity term
     }
     return uniform(o);
   };
@@ -1671,22 +1704,31 @@ __global__ void __launch_bounds__(E::NT) phase_kernel4(PhaseArgs args) {
     // barrier is the next tile's first one when it was preloaded).
     if constexpr (PH == kGram || PH == kSquare) {
       // gram: A' = g s^2 U U^T on the first iteration (X holds U), else g X X^T.
-      // square: B' = sq * (A' A' + A').
+      // square: B'' = sq * (A' A' + A') + I (the update's identity term; only
+      //   when the update has it, and only a diagonal tile has a diagonal).
       const float sc = PH == kGram ? (args.first ? s * s : 1.f) * f.g : f.sq;
       u16* O = static_cast<u16*>(PH == kGram ? d.a : d.b);
       const int rl = tile_rows<E>(tr, d.m), cl = tile_cols<E>(tc, d.m);
-      auto half = [&](auto H_) __attribute__((always_inline)) {
+      auto half = [&](auto H_, auto EYE_) __attribute__((always_inline)) {
         constexpr int H = decltype(H_)::value;
-        stage_half<E, H>(acc, epi, sc);
+        stage_half<E, H, decltype(EYE_)::value>(acc, epi, sc);
         __syncthreads();
         rows_out<E::NT>(epi, O + tr * d.lda + tc, d.lda, H, rl, cl);
         if (ti != tj) mirror_out<E::NT>(epi, O + tc * d.lda + tr, d.lda, H, rl, cl);
       };
-      half(std::integral_constant<int, 0>{});
-      __syncthreads();
-      half(std::integral_constant<int, 1>{});
+      using H0 = std::integral_constant<int, 0>;
+      using H1 = std::integral_constant<int, 1>;
+      if (PH == kSquare && f.up_diag && ti == tj) {
+        half(H0{}, std::true_type{});
+        __syncthreads();
+        half(H1{}, std::true_type{});
+      } else {
+        half(H0{}, std::false_type{});
+        __syncthreads();
+        half(H1{}, std::false_type{});
+      }
     } else {
-      // X_next = s' * a' * (X + B' X), s' = s on the first iteration.
+      // X_next = s' * a' * B'' X, s' = s on the first iteration.
       const float us = (args.first ? s : 1.f) * f.up;
       auto half = [&](auto H_) __attribute__((always_inline)) {
         constexpr int H = decltype(H_)::value;
