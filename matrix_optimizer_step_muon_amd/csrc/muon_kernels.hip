@@ -529,18 +529,24 @@ struct Engine4 {
   static_assert(DPW % 2 == 0 && 16 % PS == 0 && KK % 2 == 0 && (STAGES & (STAGES - 1)) == 0,
                 "schedule assumptions");
   // DMA issue slots. A 2-stage ring must have step kt+1's loads issued before
-  // the wait in step kt, so they all go into sub-step 0, one per 16/PS MFMAs.
-  // A deeper ring loads step kt + STAGES - 1 in step kt, needed steps later,
-  // so the loads are spread over the whole step (one per SPREAD MFMAs) and
-  // never queue up behind each other in the CU's DMA path (64 B per clock).
+  // the wait in step kt. Load d goes with MFMA 7d/4 (the first 27 MFMAs of
+  // the step): issued closer together they compete with the same sub-steps'
+  // fragment reads for LDS and the CU's memory path, issued later they arrive
+  // late. Measured on the update: one per MFMA is 2.5% slower, one per 2 MFMAs
+  // 0.4% slower, one per 2.5 or 3 MFMAs slower again, and two per MFMA right
+  // after the barrier 3% slower. A deeper ring loads step kt + STAGES - 1 in
+  // step kt, needed steps later, so the loads are spread over the whole step
+  // (one per SPREAD MFMAs).
   static constexpr bool SPREAD_ALL = STAGES >= 3;
-  static constexpr int SPREAD = SPREAD_ALL ? 16 * KK / PS : 16 / PS;
+  static constexpr int SPREAD = SPREAD_ALL ? 16 * KK / PS : 1;
+  static constexpr int SLOT_NUM = 7, SLOT_DEN = 4;  // 2-stage ring: load d at MFMA d * 7 / 4
   static constexpr int WAIT_AT = (KK - 1) * 16 + 8;  // MFMAs of a step issued before its wait
   static constexpr int DMA_BEFORE_WAIT = SPREAD_ALL ? (WAIT_AT + SPREAD - 1) / SPREAD : PS;
   // Loads that may still be in flight at the wait for step kt+1: those of
   // steps kt+2 .. kt+STAGES-2 and the ones of step kt+STAGES-1 already issued.
   static constexpr int WAIT_N = (STAGES - 3) * PS + DMA_BEFORE_WAIT;
   static_assert(!SPREAD_ALL || SPREAD * PS == 16 * KK, "spread covers the step");
+  static_assert(SPREAD_ALL || (PS - 1) * SLOT_NUM / SLOT_DEN < WAIT_AT, "every load issued before the wait");
   static MUON_INLINE int wave_m(int w) { return w >> 1; }
   static MUON_INLINE int wave_n(int w) { return w & 1; }
 
@@ -734,9 +740,18 @@ struct Engine4 {
       };
       // DMA slot of MFMA g (0 .. 16*KK - 1) of the step.
       auto dma_slot = [&](int g) __attribute__((always_inline)) {
-        if ((SPREAD_ALL || g < 16) && g % SPREAD == 0) {
-          if constexpr (TAIL) dma_any(kt + STAGES - 1, g / SPREAD);
-          else dma_cur(kt + STAGES - 1, g / SPREAD);
+        if constexpr (SPREAD_ALL) {
+          if (g % SPREAD == 0) {
+            if constexpr (TAIL) dma_any(kt + STAGES - 1, g / SPREAD);
+            else dma_cur(kt + STAGES - 1, g / SPREAD);
+          }
+        } else {
+#pragma unroll
+          for (int d = 0; d < PS; ++d)
+            if (g == d * SLOT_NUM / SLOT_DEN) {
+              if constexpr (TAIL) dma_any(kt + STAGES - 1, d);
+              else dma_cur(kt + STAGES - 1, d);
+            }
         }
       };
 #pragma unroll
