@@ -540,7 +540,12 @@ struct Engine4 {
   static constexpr bool SPREAD_ALL = STAGES >= 3;
   static constexpr int SPREAD = SPREAD_ALL ? 16 * KK / PS : 1;
   static constexpr int SLOT_NUM = 7, SLOT_DEN = 4;  // 2-stage ring: load d at MFMA d * 7 / 4
-  static constexpr int WAIT_AT = (KK - 1) * 16 + 8;  // MFMAs of a step issued before its wait
+  // The wait for step kt+1 and the barrier come after SPLIT of the last
+  // sub-step's 16 MFMAs; the other 16 - SPLIT MFMAs cover the first fragment
+  // reads of step kt+1. Measured (step time, same box): SPLIT 8 and 10 cost
+  // 0.4% and 0.5% more than 12 to 15; the update does best at 12, gram at 14.
+  static constexpr int SPLIT = QK ? 12 : 14;
+  static constexpr int WAIT_AT = (KK - 1) * 16 + SPLIT;  // MFMAs of a step issued before its wait
   static constexpr int DMA_BEFORE_WAIT = SPREAD_ALL ? (WAIT_AT + SPREAD - 1) / SPREAD : PS;
   // Loads that may still be in flight at the wait for step kt+1: those of
   // steps kt+2 .. kt+STAGES-2 and the ones of step kt+STAGES-1 already issued.
@@ -767,13 +772,13 @@ struct Engine4 {
         diag(b, kk);
         MUON_SB();
       }
-      // Last sub-step (buffer 1): half the MFMAs, then wait for this wave's
+      // Last sub-step (buffer 1): SPLIT MFMAs, then wait for this wave's
       // loads of step kt+1 and the barrier (after it every wave's loads of
       // that step are in LDS and every wave is done with this step's stage,
-      // which the next step's DMA overwrites), then the other half under the
-      // first reads of the next step.
+      // which the next step's DMA overwrites), then the other MFMAs under the
+      // 8 first reads of the next step.
 #pragma unroll
-      for (int n = 0; n < 8; ++n) {
+      for (int n = 0; n < SPLIT; ++n) {
         mf(1, n);
         dma_slot(16 * (KK - 1) + n);
         MUON_SB();
@@ -782,9 +787,11 @@ struct Engine4 {
       __syncthreads();
       MUON_SB();
 #pragma unroll
-      for (int n = 8; n < 16; ++n) {
+      for (int n = SPLIT; n < 16; ++n) {
         mf(1, n);
-        rd(0, kt + 1, 0, n - 8);
+#pragma unroll
+        for (int f = 0; f < 8; ++f)
+          if (f * (16 - SPLIT) / 8 == n - SPLIT) rd(0, kt + 1, 0, f);
         dma_slot(16 * (KK - 1) + n);
         MUON_SB();
       }
