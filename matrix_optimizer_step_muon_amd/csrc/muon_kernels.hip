@@ -491,9 +491,9 @@ MUON_INLINE Opnd uniform(const Opnd& o) {
 //
 // With one wave per SIMD nothing else hides a stalled instruction stream, so
 // the loop issues MFMAs one at a time with the rest of the work between
-// them: while MFMA n of a sub-step runs, the wave reads fragment n of the
-// next sub-step (n < 8) and, in sub-step 0, one of the DMA instructions of
-// the step STAGES - 1 ahead. Larger wave tiles read a third less LDS per flop
+// them: while MFMA n of a sub-step runs, the wave reads fragment n - 8 of the
+// next sub-step (n >= 8), and the DMA instructions of the step STAGES - 1
+// ahead are spread over the first MFMAs of the step. Larger wave tiles read a third less LDS per flop
 // than the eight-wave layout; on a power-capped chip that is worth more than
 // the latency the second wave per SIMD would hide.
 //
@@ -765,7 +765,13 @@ struct Engine4 {
 #pragma unroll
         for (int n = 0; n < 16; ++n) {
           mf(b, n);
-          if (n < 8) rd(b ^ 1, kt, kk + 1, n);
+          // The next sub-step's 8 fragments are read under this sub-step's
+          // second half: away from the DMA issue, which falls mostly in the
+          // first half (0.4% faster than reading under the first half; one
+          // read per 7/4 or 2 MFMAs is 1-2% slower).
+#pragma unroll
+          for (int f = 0; f < 8; ++f)
+            if (f + 8 == n) rd(b ^ 1, kt, kk + 1, f);
           dma_slot(16 * kk + n);
           MUON_SB();
         }
