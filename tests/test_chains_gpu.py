@@ -1,0 +1,74 @@
+"""The two-chain schedule of the bf16 four-wave engine (GEMM launches of two
+groups of matrices on two streams, forked after the norm kernel and joined by
+events).
+
+The chains run the same tiles with the same code, so one and two chains must
+give bit-identical results; and a step issued on any stream must be complete,
+for work issued after it on that stream, when that work starts.
+"""
+import os
+
+import numpy as np
+import pytest
+
+from matrix_optimizer_step_muon_amd import muon as mu
+from matrix_optimizer_step_muon_amd import workloads as wl
+
+from gpu_helpers import gpu_step, log, to_device, to_host
+
+pytestmark = pytest.mark.gpu
+
+# Several matrices of different work, so that both chains get some.
+SHAPES = [(1024, 768), (768, 1536), (512, 512), (1280, 256), (300, 700), (256, 2048)]
+
+
+def _with_chains(n, fn):
+    saved = os.environ.get("MUON_CHAINS")
+    os.environ["MUON_CHAINS"] = str(n)
+    try:
+        return fn()
+    finally:
+        if saved is None:
+            del os.environ["MUON_CHAINS"]
+        else:
+            os.environ["MUON_CHAINS"] = saved
+
+
+def test_one_and_two_chains_agree_bitwise():
+    w = wl.custom_workload("chains", SHAPES, "bf16", seed=51)
+    inputs = wl.generate(w)
+    hp = w.hparams()
+    log("case chains 1 vs 2")
+    one = _with_chains(1, lambda: gpu_step(inputs, "bf16", hp, steps=2))
+    two = _with_chains(2, lambda: gpu_step(inputs, "bf16", hp, steps=2))
+    for i, (a, b) in enumerate(zip(one, two)):
+        for name, x, y in zip(("W'", "M'", "delta"), a, b):
+            assert np.array_equal(x, y), f"matrix {i} {SHAPES[i]}: {name} differs between one and two chains"
+
+
+def test_step_on_a_side_stream_is_joined():
+    """A copy of W queued right after the step on the same (non-default)
+    stream must see the final W, in every matrix of either chain."""
+    import torch
+    w = wl.custom_workload("side_stream", SHAPES, "bf16", seed=53)
+    inputs = wl.generate(w)
+    hp = w.hparams()
+    log("case step on a side stream")
+    want = _with_chains(2, lambda: gpu_step(inputs, "bf16", hp, with_delta=False))
+
+    def run():
+        dev = [[to_device(W, "bf16"), to_device(G, "bf16"), to_device(M, "bf16")] for (W, G, M) in inputs]
+        plan = mu.Plan(dev, **hp)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            plan.step(side)
+            copies = [d[0].clone() for d in dev]   # queued behind the step on `side`
+        side.synchronize()
+        out = [to_host(c, "bf16") for c in copies]
+        plan.close()
+        return out
+
+    got = _with_chains(2, run)
+    for i, (g, ref) in enumerate(zip(got, want)):
+        assert np.array_equal(g, ref[0]), f"matrix {i} {SHAPES[i]}: W copied after the step is not the final W"
