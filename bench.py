@@ -207,6 +207,7 @@ def main():
     # so their durations do not measure the kernel; it is timed alone, in a
     # separate pass over the same inputs with one chain.
     upd_times = ktimes["update"]
+    mom_times = ktimes["momentum"]
     upd_chains = None
     if ktimes["update"][1] and ktimes["update"][1] // args.steps > wload.ns_steps and not args.no_roofline_pass:
         saved = os.environ.get("MUON_CHAINS")
@@ -227,7 +228,8 @@ def main():
             plan1.step(stream)
         torch.cuda.synchronize()
         plan1.set_timing(False)
-        upd_times = plan1.kernel_times()["update"]
+        kt1 = plan1.kernel_times()
+        upd_times, mom_times = kt1["update"], kt1["momentum"]
         upd_chains = 1
         plan1.close()
         print(f"[bench] roofline pass: {args.steps} single-chain steps", file=sys.stderr, flush=True)
@@ -245,9 +247,11 @@ def main():
     per_kernel = {k: {"avg_ms": round(v[0] / v[1], 4), "launches": v[1],
                       "ms_per_step": round(v[0] / args.steps, 4)} for k, v in ktimes.items() if v[1]}
     elem = 2 if wload.dtype == "bf16" else 4
-    mom_ms = ktimes["momentum"][0] / max(ktimes["momentum"][1], 1)
-    # Momentum kernel algorithmic bytes: read G, M; write M' and U.
-    mom_gbs = 4 * elem * wload.numel / (mom_ms / 1e3) / 1e9 if ktimes["momentum"][1] else None
+    # Momentum kernel algorithmic bytes: read G, M; write M' and U. A step
+    # runs one momentum launch per chain (or one over all matrices); its time
+    # per step, from the same pass as the update roofline, covers every element.
+    mom_ms = mom_times[0] / args.steps
+    mom_gbs = 4 * elem * wload.numel / (mom_ms / 1e3) / 1e9 if mom_times[1] else None
 
     out = {
         "metric": "Muon optimizer-step ms + achieved bf16 MFMA TFLOP/s (fraction of peak) per rank share",

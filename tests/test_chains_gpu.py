@@ -1,6 +1,7 @@
-"""The two-chain schedule of the bf16 four-wave engine (GEMM launches of two
-groups of matrices on two streams, forked after the norm kernel and joined by
-events).
+"""The two-chain schedule of the bf16 four-wave engine: two groups of matrices,
+each with its own momentum, norm and GEMM launches on its own stream, forked at
+the start of the step and joined by events. (MUON_SPLIT_PROLOGUE=0 runs one
+momentum and one norm kernel over all matrices before the fork instead.)
 
 The chains run the same tiles with the same code, so one and two chains must
 give bit-identical results; and a step issued on any stream must be complete,
@@ -22,25 +23,31 @@ pytestmark = pytest.mark.gpu
 SHAPES = [(1024, 768), (768, 1536), (512, 512), (1280, 256), (300, 700), (256, 2048)]
 
 
-def _with_chains(n, fn):
-    saved = os.environ.get("MUON_CHAINS")
-    os.environ["MUON_CHAINS"] = str(n)
+def _with_env(name, value, fn):
+    saved = os.environ.get(name)
+    os.environ[name] = str(value)
     try:
         return fn()
     finally:
         if saved is None:
-            del os.environ["MUON_CHAINS"]
+            del os.environ[name]
         else:
-            os.environ["MUON_CHAINS"] = saved
+            os.environ[name] = saved
 
 
-def test_one_and_two_chains_agree_bitwise():
+def _with_chains(n, fn):
+    return _with_env("MUON_CHAINS", n, fn)
+
+
+@pytest.mark.parametrize("split_prologue", [1, 0])
+def test_one_and_two_chains_agree_bitwise(split_prologue):
     w = wl.custom_workload("chains", SHAPES, "bf16", seed=51)
     inputs = wl.generate(w)
     hp = w.hparams()
-    log("case chains 1 vs 2")
+    log(f"case chains 1 vs 2, split prologue {split_prologue}")
     one = _with_chains(1, lambda: gpu_step(inputs, "bf16", hp, steps=2))
-    two = _with_chains(2, lambda: gpu_step(inputs, "bf16", hp, steps=2))
+    two = _with_env("MUON_SPLIT_PROLOGUE", split_prologue,
+                    lambda: _with_chains(2, lambda: gpu_step(inputs, "bf16", hp, steps=2)))
     for i, (a, b) in enumerate(zip(one, two)):
         for name, x, y in zip(("W'", "M'", "delta"), a, b):
             assert np.array_equal(x, y), f"matrix {i} {SHAPES[i]}: {name} differs between one and two chains"
