@@ -16,7 +16,11 @@ Timing follows the pages' protocol of averaging many steps (Canzona analysis
 page, section 5, "Metrics"): W untimed warm-up steps, then exactly K steps
 between two device synchronisations, timed with events on the step's stream.
 Per-kernel durations come from HIP event pairs that the library records around
-every launch during the same timed region, on the same stream.
+every launch during the same timed region, on the same stream. After it,
+--runs fresh plans each run 3 warm-up and --run-steps timed steps (the pages'
+average over runs of several steps); the line reports their mean, median and
+min. The GPU's graphics clock and socket power are sampled through amdsmi
+during both, because the chip runs at its power cap and its clock varies.
 
 It prints one JSON line, with value = algorithmic TFLOP/s of the whole step.
 Flops count only the triangles the method needs (see oracle.step_flops).
@@ -30,6 +34,7 @@ import math
 import os
 import platform
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -54,6 +59,10 @@ def parse():
                     help="GEMM chains of the plan (sets MUON_CHAINS; 0: the library default)")
     ap.add_argument("--no-roofline-pass", action="store_true",
                     help="skip the separate single-chain pass that times the update kernel alone")
+    ap.add_argument("--runs", type=int, default=10,
+                    help="protocol runs after the timed region: each a fresh plan, 3 warm-up and "
+                         "--run-steps timed steps (0: none)")
+    ap.add_argument("--run-steps", type=int, default=10)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain elementwise copy kernel (torch.add, fp32) over this "
                          "many MiB, the reference for scaling HBM byte counters")
@@ -99,6 +108,111 @@ def cpu_baseline(wload, indices):
             "kind": "oracle", "seconds": round(dt, 3),
             "sample": f"fp64 numpy oracle, full step on {len(indices)} of {len(wload.shapes)} "
                       f"matrices ({', '.join(shapes)}) of the same workload"}
+
+
+class GpuSampler:
+    """Samples the graphics clock and socket power of the GPU in use through
+    amdsmi (the library under rocm-smi), on a background thread, while a `with`
+    block runs. Best effort: where amdsmi or the device's metrics cannot be
+    read, summary() says why instead."""
+
+    def __init__(self, device_props, period_s=0.01):
+        self.props = device_props
+        self.period = period_s
+        self.samples = []
+        self.error = None
+        self._stop = threading.Event()
+        self._thread = None
+        self._smi = None
+
+    def _handle(self, smi):
+        handles = smi.amdsmi_get_processor_handles()
+        want = (getattr(self.props, "pci_domain_id", None), getattr(self.props, "pci_bus_id", None),
+                getattr(self.props, "pci_device_id", None))
+        for h in handles:
+            try:
+                dom, bus, rest = smi.amdsmi_get_gpu_device_bdf(h).split(":")
+                if (int(dom, 16), int(bus, 16), int(rest.split(".")[0], 16)) == want:
+                    return h
+            except Exception:
+                continue
+        if len(handles) == 1:
+            return handles[0]
+        raise RuntimeError(f"no amdsmi device matches PCI {want} among {len(handles)}")
+
+    def __enter__(self):
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self._smi = amdsmi
+            self._h = self._handle(amdsmi)
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+        except Exception as e:  # noqa: BLE001 - any failure only disables sampling
+            self.error = f"{type(e).__name__}: {e}"[:200]
+        return self
+
+    def _run(self):
+        smi = self._smi
+        while not self._stop.is_set():
+            try:
+                clk = smi.amdsmi_get_clock_info(self._h, smi.AmdSmiClkType.GFX)["clk"]
+                pw = smi.amdsmi_get_power_info(self._h)
+                self.samples.append((clk, pw.get("current_socket_power"), pw.get("power_limit")))
+            except Exception as e:  # noqa: BLE001
+                self.error = f"{type(e).__name__}: {e}"[:200]
+                return
+            self._stop.wait(self.period)
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread is not None:
+            self._thread.join()
+        if self._smi is not None:
+            try:
+                self._smi.amdsmi_shut_down()
+            except Exception:  # noqa: BLE001
+                pass
+        return False
+
+    def summary(self):
+        import numpy as np
+        clk = [c for c, _, _ in self.samples if isinstance(c, (int, float))]
+        if not clk:
+            return {"source": "amdsmi", "samples": 0, "error": self.error or "no samples"}
+        pw = [p for _, p, _ in self.samples if isinstance(p, (int, float))]
+        lim = [q for _, _, q in self.samples if isinstance(q, (int, float))]
+        limit = lim[-1] if lim else None
+        if limit is not None and limit > 1e5:  # reported in microwatts
+            limit = limit / 1e6
+        return {"source": "amdsmi (the rocm-smi library): GFX clock and socket power, polled every "
+                          "10 ms during the protocol runs",
+                "samples": len(clk), "gfx_mhz_median": float(np.median(clk)),
+                "gfx_mhz_min": min(clk), "gfx_mhz_max": max(clk),
+                "socket_power_w_median": float(np.median(pw)) if pw else None,
+                "power_limit_w": limit}
+
+
+def protocol_runs(mu, dev, hparams, stream, runs, steps, warmup=3):
+    """The pages' averaging protocol: `runs` fresh plans in this process, each
+    with `warmup` untimed and `steps` timed consecutive steps on the same
+    buffers. Returns the per-step times in ms."""
+    import torch
+    times = []
+    for _ in range(runs):
+        plan = mu.Plan(dev, **hparams)
+        for _ in range(warmup):
+            plan.step(stream)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        ev[0].record(stream)
+        for k in range(steps):
+            plan.step(stream)
+            ev[k + 1].record(stream)
+        torch.cuda.synchronize()
+        times += [ev[k].elapsed_time(ev[k + 1]) for k in range(steps)]
+        plan.close()
+    return times
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "update_kernel_traffic_qwen3_32b_layer.txt")
@@ -234,6 +348,22 @@ def main():
         plan1.close()
         print(f"[bench] roofline pass: {args.steps} single-chain steps", file=sys.stderr, flush=True)
 
+    # The pages' protocol (runs x steps, each run a fresh plan), with the clock
+    # sampled over its span of several seconds (the device's metrics refresh
+    # too slowly to be sampled over the shorter timed region above).
+    proto = None
+    clock = None
+    if args.runs > 0 and args.run_steps > 0:
+        psampler = GpuSampler(torch.cuda.get_device_properties(0))
+        with psampler:
+            pt = protocol_runs(mu, dev, wload.hparams(), stream, args.runs, args.run_steps)
+        proto = {"runs": args.runs, "steps_per_run": args.run_steps, "warmup_per_run": 3,
+                 "mean_ms": round(float(np.mean(pt)), 4), "median_ms": round(float(np.median(pt)), 4),
+                 "min_ms": round(min(pt), 4), "max_ms": round(max(pt), 4)}
+        clock = psampler.summary()
+        print(f"[bench] protocol: {args.runs} runs x {args.run_steps} steps, mean {proto['mean_ms']:.3f} ms",
+              file=sys.stderr, flush=True)
+
     fl = nsflops(wload.shapes, wload.ns_steps)
     tflops = fl["total"] / (ms_per_step / 1e3) / 1e12
     peak = BF16_PEAK_TFLOPS if wload.dtype == "bf16" else F32_PEAK_TFLOPS
@@ -275,6 +405,13 @@ def main():
         "step_ms": {"mean": round(ms_per_step, 4), "median": round(float(np.median(step_ms)), 4),
                     "min": round(min(step_ms), 4), "max": round(max(step_ms), 4)},
         "dense_equiv_tflops": round(fl["dense"] / (ms_per_step / 1e3) / 1e12, 2),
+        "protocol": proto,
+        "gpu_clock": clock,
+        # The same rate against the dense peak scaled to the observed clock
+        # (the published peak assumes 2.4 GHz; the chip runs at its power cap).
+        "fraction_of_peak_at_observed_clock": (
+            round(tflops / (peak * clock["gfx_mhz_median"] / 2400.0), 4)
+            if clock and clock.get("gfx_mhz_median") else None),
         "roofline": {
             "kernel": "update (X' = aX + BX; weight apply on the last iteration)",
             "bound": "mfma",
