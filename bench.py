@@ -63,6 +63,8 @@ def parse():
                     help="protocol runs after the timed region: each a fresh plan, 3 warm-up and "
                          "--run-steps timed steps (0: none)")
     ap.add_argument("--run-steps", type=int, default=10)
+    ap.add_argument("--no-tp-apply", action="store_true",
+                    help="skip the measurement of the tensor-parallel local update (muon_apply)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain elementwise copy kernel (torch.add, fp32) over this "
                          "many MiB, the reference for scaling HBM byte counters")
@@ -215,6 +217,51 @@ def protocol_runs(mu, dev, hparams, stream, runs, steps, warmup=3):
     return times
 
 
+# Split kind of each matrix of a Qwen3 layer (q, k, v, o, gate, up, down):
+# q, k, v, gate and up are column-parallel, o and down row-parallel.
+QWEN3_LAYER_KINDS = ("column", "column", "column", "row", "column", "column", "row")
+
+
+def tp_apply_measure(mu, shapes, dtype, stream, ranks=8, reps=20):
+    """The tensor-parallel local update P_local += Delta W_local over every
+    rank's shards of the given matrices (all ranks on this one GPU, so the
+    shards cover the whole matrices), as one muon_apply launch. Inputs are
+    resident; returns the average launch time and its HBM rate on the
+    algorithmic bytes (read P and Delta W, write P)."""
+    import torch
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    elem = 2 if dtype == "bf16" else 4
+    pairs, keep, numel = [], [], 0
+    for i, (r, c) in enumerate(shapes):
+        kind = QWEN3_LAYER_KINDS[i % len(QWEN3_LAYER_KINDS)]
+        D = torch.randn(r, c, device="cuda", dtype=torch.float32).mul_(4e-4).to(dt)
+        keep.append(D)
+        n = r if kind == "column" else c
+        for k in range(ranks):
+            a, b = k * n // ranks, (k + 1) * n // ranks
+            view = D[a:b, :] if kind == "column" else D[:, a:b]
+            P = torch.randn(view.shape, device="cuda", dtype=torch.float32).mul_(0.02).to(dt)
+            pairs.append((P, view))
+            numel += P.numel()
+    plan = mu.ApplyPlan(pairs)
+    plan.apply(stream)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        plan.apply(stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    plan.close()
+    gbs = 3 * elem * numel / (ms / 1e3) / 1e9
+    return {"shards": len(pairs), "ranks": ranks, "elements": numel, "avg_launch_ms": round(ms, 4),
+            "alg_bytes_per_elem": 3 * elem, "achieved_gbs": round(gbs, 1), "peak_gbs": HBM_PEAK_GBS,
+            "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "what": f"P_local += Delta W_local over all {ranks} ranks' TP shards of the workload's "
+                    "matrices (column-parallel: row blocks; row-parallel: column blocks, strided views)"}
+
+
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "update_kernel_traffic_qwen3_32b_layer.txt")
 KERNEL_SOURCE = os.path.join(ROOT, "matrix_optimizer_step_muon_amd", "csrc", "muon_kernels.hip")
 
@@ -364,6 +411,12 @@ def main():
         print(f"[bench] protocol: {args.runs} runs x {args.run_steps} steps, mean {proto['mean_ms']:.3f} ms",
               file=sys.stderr, flush=True)
 
+    tp_apply = None
+    if not args.no_tp_apply:
+        tp_apply = tp_apply_measure(mu, wload.shapes, wload.dtype, stream)
+        print(f"[bench] tp apply: {tp_apply['avg_launch_ms']:.3f} ms, {tp_apply['achieved_gbs']:.0f} GB/s",
+              file=sys.stderr, flush=True)
+
     fl = nsflops(wload.shapes, wload.ns_steps)
     tflops = fl["total"] / (ms_per_step / 1e3) / 1e12
     peak = BF16_PEAK_TFLOPS if wload.dtype == "bf16" else F32_PEAK_TFLOPS
@@ -428,6 +481,7 @@ def main():
             "avg_launch_ms": round(upd_avg, 4),
         },
         "kernels": per_kernel,
+        "tp_apply": tp_apply,
         "momentum_hbm": {"achieved_gbs": round(mom_gbs, 1) if mom_gbs else None,
                          "peak_gbs": HBM_PEAK_GBS, "alg_bytes_per_elem": 4 * elem},
         "device": torch.cuda.get_device_name(0),

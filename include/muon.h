@@ -152,6 +152,63 @@ muon_status muon_plan_reset_timing(muon_plan_t plan);
  * grid[k]    = workgroups launched per launch of kind k. */
 muon_status muon_plan_info(muon_plan_t plan, int64_t* n_tiles, int64_t* grid);
 
+/* ---------------------------------------------------------------------------
+ * Tensor-parallel local update.
+ *
+ * Under tensor parallelism a rank holds shards of each weight matrix: a
+ * column-parallel layer splits the output dimension (a block of rows of the
+ * rows x cols W), a row-parallel layer the input dimension (a block of
+ * columns) (Canzona analysis page, section 2, "The Core Problem"). The host
+ * rank of a tensor runs muon_step on the whole matrix with delta set (and w
+ * NULL); the update is then cut into the TP partition's slices, and every rank
+ * adds its slices to its parameter shards, P_local <- P_local + Delta W_local,
+ * element by element and with no communication (section 3.4, "The TP Task
+ * Abstraction", micro-group lifecycle, steps 3 and 4).
+ *
+ * One shard: p and d are device pointers of the plan's dtype.
+ * p     the local parameter shard, rows x cols, row stride ldp elements,
+ *       updated in place;
+ * d     its update slice, rows x cols, row stride ldd elements, read only
+ *       (a view into a delta matrix, or a buffer the shard arrived in).
+ * A column block of a row-major matrix is such a view: its first element and
+ * the matrix's row stride. */
+typedef struct {
+  void* p;
+  const void* d;
+  int64_t rows;
+  int64_t cols;
+  int64_t ldp;
+  int64_t ldd;
+} muon_shard;
+
+typedef struct muon_apply_plan_s* muon_apply_plan_t;
+
+/* Builds a static plan over n shards; the TP layout is fixed at
+ * initialisation, as the pages' assignment of tensors is. shards is a host
+ * array; the plan keeps the device pointers. Every argument is validated
+ * before any HIP call. Errors: INVALID_ARG (n < 1, null pointers, rows or
+ * cols < 1 or > 2^24, ldp or ldd < cols, more than 2^31 - 1 tiles of 64 x 64),
+ * ALIGN (p or d not aligned to the element size), ALIAS (an element of a p
+ * view is also in another p view or in a d view; d views may share elements),
+ * UNSUPPORTED (dtype). Two views with the same row stride are checked element
+ * by element (column blocks of one matrix are disjoint); views with different
+ * strides whose address ranges overlap are rejected. Then the plan copies its
+ * shard table to the current device: HIP or OOM on failure. The call
+ * synchronises the device once, at its end. */
+muon_status muon_apply_plan(const muon_shard* shards, int32_t n, int32_t dtype,
+                            muon_apply_plan_t* out);
+
+/* Enqueues P_local <- P_local + Delta W_local for every shard of the plan on
+ * `stream` (a hipStream_t; NULL is the null stream): one kernel, no
+ * allocation, no host synchronisation. Each sum is formed in fp32 and stored
+ * once (bf16: round to nearest even), which for two values of the storage type
+ * is their exactly rounded sum. Shards are independent and the result does not
+ * depend on their order. */
+muon_status muon_apply(muon_apply_plan_t plan, void* stream);
+
+/* Frees the plan. NULL is a no-op. Synchronises the device. */
+muon_status muon_apply_plan_destroy(muon_apply_plan_t plan);
+
 #ifdef __cplusplus
 }
 #endif

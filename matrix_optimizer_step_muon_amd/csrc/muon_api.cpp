@@ -605,3 +605,160 @@ muon_status muon_plan_destroy(muon_plan_t p) {
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------- TP shard apply
+
+struct muon_apply_plan_s {
+  int dtype = 1;
+  int n = 0;
+  int device = 0;
+  void* ws = nullptr;
+  muon::ShardDev* d_shards = nullptr;
+  int32_t* d_prefix = nullptr;
+  int32_t blocks = 0;
+};
+
+namespace {
+
+// A strided view: element (i, j), i < rows, j < cols, at base + (i*ld + j)*elem.
+struct View { uintptr_t base; int64_t rows, cols, ld; int shard; const char* what; };
+
+uintptr_t view_end(const View& v, size_t elem) {
+  return v.base + uintptr_t(((v.rows - 1) * v.ld + v.cols) * int64_t(elem));
+}
+
+// Whether two views share an element. Views with the same row stride (and an
+// offset that is a whole number of elements) are compared by their row and
+// column ranges; other views whose address ranges overlap count as sharing.
+bool views_share(const View& a, const View& b, size_t elem) {
+  if (view_end(a, elem) <= b.base || view_end(b, elem) <= a.base) return false;
+  if (a.ld != b.ld) return true;
+  const View& lo = a.base <= b.base ? a : b;
+  const View& hi = a.base <= b.base ? b : a;
+  const uintptr_t off = hi.base - lo.base;
+  if (off % elem != 0) return true;
+  const int64_t e = int64_t(off / elem), dr = e / lo.ld, dc = e % lo.ld;
+  if (dc + hi.cols > lo.ld) return true;  // hi's rows wrap into lo's next row
+  const bool rows_meet = dr < lo.rows;    // hi starts dr rows below lo
+  const bool cols_meet = dc < lo.cols;    // and dc columns to the right
+  return rows_meet && cols_meet;
+}
+
+muon_status validate_shards(const muon_shard* sh, int32_t n, int32_t dtype) {
+  if (!sh) return fail(MUON_ERR_INVALID_ARG, "shards is NULL");
+  if (n < 1) return fail(MUON_ERR_INVALID_ARG, "n must be >= 1");
+  if (dtype != MUON_F32 && dtype != MUON_BF16) return fail(MUON_ERR_UNSUPPORTED, "dtype must be MUON_F32 or MUON_BF16");
+  const size_t elem = dtype == MUON_BF16 ? 2 : 4;
+  std::vector<View> ps, ds;
+  int64_t tiles = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const muon_shard& s = sh[i];
+    const std::string at = "shard " + std::to_string(i) + ": ";
+    if (!s.p || !s.d) return fail(MUON_ERR_INVALID_ARG, at + "p or d is NULL");
+    if (s.rows < 1 || s.cols < 1) return fail(MUON_ERR_INVALID_ARG, at + "rows and cols must be >= 1");
+    if (s.rows > kMaxDim || s.cols > kMaxDim) return fail(MUON_ERR_INVALID_ARG, at + "rows and cols must be <= 2^24");
+    if (s.ldp < s.cols || s.ldd < s.cols) return fail(MUON_ERR_INVALID_ARG, at + "ldp and ldd must be >= cols");
+    if (s.ldp > (int64_t(1) << 40) || s.ldd > (int64_t(1) << 40)) return fail(MUON_ERR_INVALID_ARG, at + "row stride too large");
+    if (reinterpret_cast<uintptr_t>(s.p) % elem || reinterpret_cast<uintptr_t>(s.d) % elem)
+      return fail(MUON_ERR_ALIGN, at + "p or d is not aligned to the element size");
+    tiles += ((s.rows + muon::kEwTile - 1) / muon::kEwTile) * ((s.cols + muon::kEwTile - 1) / muon::kEwTile);
+    if (tiles > INT32_MAX) return fail(MUON_ERR_INVALID_ARG, "more than 2^31 - 1 tiles");
+    ps.push_back({reinterpret_cast<uintptr_t>(s.p), s.rows, s.cols, s.ldp, i, "p"});
+    ds.push_back({reinterpret_cast<uintptr_t>(s.d), s.rows, s.cols, s.ldd, i, "d"});
+  }
+  // Written views against written and read views: sort everything by start,
+  // and compare each written view with the views that start before it ends.
+  std::vector<View> all(ps);
+  all.insert(all.end(), ds.begin(), ds.end());
+  std::sort(all.begin(), all.end(), [](const View& x, const View& y) { return x.base < y.base; });
+  for (size_t a = 0; a < all.size(); ++a) {
+    const uintptr_t end = view_end(all[a], elem);
+    for (size_t b = a + 1; b < all.size() && all[b].base < end; ++b) {
+      const bool written = all[a].what[0] == 'p' || all[b].what[0] == 'p';
+      if (!written) continue;
+      if (views_share(all[a], all[b], elem))
+        return fail(MUON_ERR_ALIAS, "shard " + std::to_string(all[a].shard) + " " + all[a].what + " overlaps shard " +
+                                        std::to_string(all[b].shard) + " " + all[b].what);
+    }
+  }
+  return MUON_OK;
+}
+
+void free_apply_plan(muon_apply_plan_s* p) {
+  if (!p) return;
+  if (p->ws) (void)hipFree(p->ws);
+  delete p;
+}
+
+}  // namespace
+
+extern "C" {
+
+muon_status muon_apply_plan(const muon_shard* shards, int32_t n, int32_t dtype, muon_apply_plan_t* out) {
+  if (!out) return fail(MUON_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  muon_status st = validate_shards(shards, n, dtype);
+  if (st != MUON_OK) return st;
+  const size_t elem = dtype == MUON_BF16 ? 2 : 4;
+  std::vector<muon::ShardDev> h(n);
+  std::vector<int32_t> prefix(n + 1, 0);
+  for (int32_t i = 0; i < n; ++i) {
+    const muon_shard& s = shards[i];
+    muon::ShardDev& d = h[i];
+    d.p = s.p;
+    d.d = s.d;
+    d.ldp = s.ldp;
+    d.ldd = s.ldd;
+    d.rows = int32_t(s.rows);
+    d.cols = int32_t(s.cols);
+    d.tiles_c = int32_t((s.cols + muon::kEwTile - 1) / muon::kEwTile);
+    const uintptr_t va = 4 * elem;
+    d.vec = s.cols % 4 == 0 && s.ldp % 4 == 0 && s.ldd % 4 == 0 && reinterpret_cast<uintptr_t>(s.p) % va == 0 &&
+            reinterpret_cast<uintptr_t>(s.d) % va == 0;
+    const int32_t tr = int32_t((s.rows + muon::kEwTile - 1) / muon::kEwTile);
+    prefix[i + 1] = prefix[i] + tr * d.tiles_c;
+  }
+  auto* p = new muon_apply_plan_s();
+  p->dtype = dtype;
+  p->n = n;
+  p->blocks = prefix[n];
+  hipError_t e = hipGetDevice(&p->device);
+  if (e != hipSuccess) { free_apply_plan(p); return hip_fail(e, "hipGetDevice"); }
+  const size_t o_prefix = round_up(sizeof(muon::ShardDev) * n, 256);
+  const size_t bytes = o_prefix + sizeof(int32_t) * (n + 1);
+  e = hipMalloc(&p->ws, bytes);
+  if (e != hipSuccess) {
+    p->ws = nullptr;
+    free_apply_plan(p);
+    (void)hipGetLastError();
+    return fail(MUON_ERR_OOM, "hipMalloc of " + std::to_string(bytes) + " bytes failed");
+  }
+  p->d_shards = static_cast<muon::ShardDev*>(p->ws);
+  p->d_prefix = reinterpret_cast<int32_t*>(static_cast<char*>(p->ws) + o_prefix);
+  e = hipMemcpy(p->d_shards, h.data(), sizeof(muon::ShardDev) * n, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(p->d_prefix, prefix.data(), sizeof(int32_t) * (n + 1), hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) { free_apply_plan(p); return hip_fail(e, "hipMemcpy"); }
+  *out = p;
+  return MUON_OK;
+}
+
+muon_status muon_apply(muon_apply_plan_t p, void* stream) {
+  if (!p) return fail(MUON_ERR_INVALID_ARG, "plan is NULL");
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (cur != p->device && (e = hipSetDevice(p->device)) != hipSuccess) return hip_fail(e, "hipSetDevice");
+  e = muon::launch_shard_apply(p->dtype, p->d_shards, p->d_prefix, p->n, p->blocks, static_cast<hipStream_t>(stream));
+  if (cur != p->device) (void)hipSetDevice(cur);
+  return e == hipSuccess ? MUON_OK : hip_fail(e, "kernel launch");
+}
+
+muon_status muon_apply_plan_destroy(muon_apply_plan_t p) {
+  if (!p) return MUON_OK;
+  hipError_t e = hipDeviceSynchronize();
+  free_apply_plan(p);
+  return e == hipSuccess ? MUON_OK : hip_fail(e, "hipDeviceSynchronize");
+}
+
+}  // extern "C"

@@ -87,11 +87,25 @@ struct EwArgs {
   StepCoeffs co;
 };
 
+// One view of the TP shard apply (P += D over rows x cols, row strides ldp
+// and ldd). The kernel runs one kEwTile x kEwTile tile per workgroup.
+struct ShardDev {
+  void* p;
+  const void* d;
+  int64_t ldp, ldd;
+  int32_t rows, cols;
+  int32_t tiles_c;  // ceil(cols / kEwTile)
+  int32_t vec;      // cols, ldp, ldd multiples of 4 and both pointers 4-element aligned
+};
+
 // Launchers (muon_kernels.hip). dtype: 0 = fp32, 1 = bf16.
 hipError_t launch_momentum(int dtype, const EwArgs& args, int32_t n_blocks, hipStream_t s);
 hipError_t launch_norm(const MatDev* mats, const float* partials, float* scale, int32_t n_mats,
                        float eps, hipStream_t s);
 hipError_t launch_apply(int dtype, const EwArgs& args, int32_t n_blocks, hipStream_t s);
+// prefix[i] = first tile of shard i (prefix[n] = n_blocks).
+hipError_t launch_shard_apply(int dtype, const ShardDev* shards, const int32_t* prefix, int32_t n,
+                              int32_t n_blocks, hipStream_t s);
 // bf16 GEMM engine pipelines: 8 waves of 128 x 64 with K step 64 and a ring
 // of 2 LDS stages, or K step 32 and 4 stages; 4 waves of 128 x 128 with K
 // step 64 and 2 stages, or K step 32 and 4 stages.

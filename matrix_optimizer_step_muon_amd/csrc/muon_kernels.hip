@@ -1937,6 +1937,43 @@ __global__ void __launch_bounds__(256) apply_kernel(EwArgs args) {
   }
 }
 
+// TP local update: P += D over strided views, one 64 x 64 tile per workgroup
+// of 256 threads (4 rows of 4 elements each). Each sum is formed in fp32 and
+// stored once; for two bf16 (or fp32) values that is their exactly rounded
+// sum.
+template <class T>
+__global__ void __launch_bounds__(256) shard_apply_kernel(const ShardDev* shards, const int32_t* prefix,
+                                                          int n) {
+  constexpr int TS = kEwTile;
+  const int si = find_mat(prefix, n, blockIdx.x);
+  const auto& s = kconst(shards)[si];
+  const int local = blockIdx.x - prefix[si];
+  const int64_t r0 = (int64_t)(local / s.tiles_c) * TS;
+  const int64_t c0 = (int64_t)(local % s.tiles_c) * TS;
+  T* P = static_cast<T*>(s.p);
+  const T* D = static_cast<const T*>(s.d);
+  const int rows = s.rows, cols = s.cols;
+  const int64_t ldp = s.ldp, ldd = s.ldd;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t gr = r0 + q * 16 + (tid >> 4), gc = c0 + (tid & 15) * 4;
+    if (gr >= rows) continue;
+    T* pp = P + gr * ldp + gc;
+    const T* dd = D + gr * ldd + gc;
+    if (s.vec && gc + 3 < cols) {
+      float a[4], b[4];
+      Vec4<T>::load(pp, a);
+      Vec4<T>::load(dd, b);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a[e] += b[e];
+      Vec4<T>::store(pp, a);
+    } else {
+      for (int e = 0; e < 4 && gc + e < cols; ++e) Elem<T>::store(pp + e, Elem<T>::load(pp + e) + Elem<T>::load(dd + e));
+    }
+  }
+}
+
 // ------------------------------------------------------------ launchers
 
 hipError_t launch_momentum(int dtype, const EwArgs& args, int32_t n_blocks, hipStream_t s) {
@@ -1948,6 +1985,13 @@ hipError_t launch_momentum(int dtype, const EwArgs& args, int32_t n_blocks, hipS
 hipError_t launch_norm(const MatDev* mats, const float* partials, float* scale, int32_t n_mats,
                        float eps, hipStream_t s) {
   hipLaunchKernelGGL(norm_kernel, dim3(n_mats), dim3(256), 0, s, mats, partials, scale, eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_shard_apply(int dtype, const ShardDev* shards, const int32_t* prefix, int32_t n,
+                              int32_t n_blocks, hipStream_t s) {
+  if (dtype == 1) hipLaunchKernelGGL(shard_apply_kernel<u16>, dim3(n_blocks), dim3(256), 0, s, shards, prefix, n);
+  else hipLaunchKernelGGL(shard_apply_kernel<float>, dim3(n_blocks), dim3(256), 0, s, shards, prefix, n);
   return hipGetLastError();
 }
 

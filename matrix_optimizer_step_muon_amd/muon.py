@@ -27,6 +27,11 @@ class muon_matrix(ctypes.Structure):
                 ("delta", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64)]
 
 
+class muon_shard(ctypes.Structure):
+    _fields_ = [("p", ctypes.c_void_p), ("d", ctypes.c_void_p), ("rows", ctypes.c_int64),
+                ("cols", ctypes.c_int64), ("ldp", ctypes.c_int64), ("ldd", ctypes.c_int64)]
+
+
 class muon_hparams(ctypes.Structure):
     _fields_ = [("lr", ctypes.c_float), ("beta", ctypes.c_float), ("eps", ctypes.c_float),
                 ("a", ctypes.c_float), ("b", ctypes.c_float), ("c", ctypes.c_float),
@@ -45,7 +50,8 @@ _lib = None
 # Every function the header declares.
 EXPORTS = ("muon_hparams_default", "muon_plan", "muon_plan_workspace_bytes", "muon_step",
            "muon_plan_destroy", "muon_last_error", "muon_plan_set_timing",
-           "muon_plan_kernel_times", "muon_plan_reset_timing", "muon_plan_info")
+           "muon_plan_kernel_times", "muon_plan_reset_timing", "muon_plan_info",
+           "muon_apply_plan", "muon_apply", "muon_apply_plan_destroy")
 
 
 def lib() -> ctypes.CDLL:
@@ -70,6 +76,9 @@ def lib() -> ctypes.CDLL:
     L.muon_plan_kernel_times.argtypes = [c_vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(c_i64)]
     L.muon_plan_reset_timing.argtypes = [c_vp]
     L.muon_plan_info.argtypes = [c_vp, ctypes.POINTER(c_i64), ctypes.POINTER(c_i64)]
+    L.muon_apply_plan.argtypes = [ctypes.POINTER(muon_shard), c_i32, c_i32, ctypes.POINTER(c_vp)]
+    L.muon_apply.argtypes = [c_vp, c_vp]
+    L.muon_apply_plan_destroy.argtypes = [c_vp]
     for name in EXPORTS:
         if name != "muon_last_error":
             getattr(L, name).restype = c_int
@@ -192,6 +201,62 @@ class Plan:
         if self._handle is not None:
             h, self._handle = self._handle, None
             destroy_raw(h)
+        self._tensors = []
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+
+class ApplyPlan:
+    """A static plan of the tensor-parallel local update P += Delta W over a
+    list of ``(P, D)`` device tensors: 2-D, one dtype (bf16 or fp32), unit
+    column stride (row-major views, such as a column block of a larger matrix,
+    are fine). P is updated in place; D is read. The plan keeps the tensors
+    referenced, since it keeps their addresses."""
+
+    def __init__(self, pairs: Iterable[Sequence]):
+        self._handle = None
+        self._tensors: List = []
+        descs = []
+        dtype = None
+        for P, D in pairs:
+            for t in (P, D):
+                if not t.is_cuda or t.dim() != 2 or t.stride(1) != 1:
+                    raise MuonError(-1, "shards must be 2-D device tensors with unit column stride")
+            code = _dtype_code(P)
+            dtype = code if dtype is None else dtype
+            if _dtype_code(D) != dtype or code != dtype or tuple(P.shape) != tuple(D.shape):
+                raise MuonError(-1, "P and D of every shard must share one dtype and shape")
+            self._tensors.append((P, D))
+            descs.append(muon_shard(P.data_ptr(), D.data_ptr(), P.shape[0], P.shape[1],
+                                    P.stride(0), D.stride(0)))
+        if not descs:
+            raise MuonError(-1, "no shards")
+        arr = (muon_shard * len(descs))(*descs)
+        out = ctypes.c_void_p()
+        check(lib().muon_apply_plan(arr, len(descs), dtype, ctypes.byref(out)))
+        self._handle = out.value
+
+    def apply(self, stream=None) -> None:
+        import torch
+        if stream is None:
+            stream = torch.cuda.current_stream()
+        check(lib().muon_apply(ctypes.c_void_p(self._handle),
+                               ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))))
+
+    def close(self) -> None:
+        if self._handle is not None:
+            h, self._handle = self._handle, None
+            check(lib().muon_apply_plan_destroy(ctypes.c_void_p(h)))
         self._tensors = []
 
     def __del__(self):

@@ -39,7 +39,9 @@ Pins (tests/test_oracle_pins.py, all on the CPU):
 - cubic Newton-Schulz converging to the polar factor;
 - transpose equivariance and scale invariance;
 - semi-orthogonal and rank-1 closed forms;
-- the T = 0 and zero-input special cases, and where eps sits.
+- the T = 0 and zero-input special cases, and where eps sits;
+- the TP partition covers every element of a weight exactly once, and the
+  shard-by-shard local update reassembles the whole-matrix sum (brute force).
 Every function here has at least one pin.
 """
 
@@ -164,3 +166,34 @@ def step_flops(rows: int, cols: int, ns_steps: int = DEFAULT_NS_STEPS) -> int:
     """
     m, n = min(rows, cols), max(rows, cols)
     return ns_steps * (m * (m + 1) * n + m * m * (m + 1) + 2 * m * m * n)
+
+
+def tp_shard_ranges(rows: int, cols: int, ranks: int, kind: str):
+    """The tensor-parallel partition of a rows x cols (out, in) weight over
+    ``ranks`` ranks, as ``[(row_slice, col_slice)]`` per rank.
+
+    A column-parallel layer splits the output dimension (the rows), a
+    row-parallel layer the input dimension (the columns) (Canzona analysis page,
+    section 2, "The Core Problem"). The pages do not say how a dimension that
+    is not a multiple of the rank count is split; rank r takes
+    [r*n // ranks, (r+1)*n // ranks), so sizes differ by at most one.
+    """
+    if kind not in ("column", "row"):
+        raise ValueError("kind must be 'column' or 'row'")
+    n = rows if kind == "column" else cols
+    cuts = [r * n // ranks for r in range(ranks + 1)]
+    out = []
+    for r in range(ranks):
+        part = slice(cuts[r], cuts[r + 1])
+        out.append((part, slice(0, cols)) if kind == "column" else (slice(0, rows), part))
+    return out
+
+
+def apply_shard(P: np.ndarray, D: np.ndarray) -> np.ndarray:
+    """The local update of one shard, ``P_local + Delta W_local``, element by
+    element (Canzona analysis page, section 3.4, "The TP Task Abstraction",
+    micro-group lifecycle step 4), in float64. The caller rounds the result to
+    the storage type."""
+    if P.shape != D.shape:
+        raise ValueError("P and D must have one shape")
+    return P + D

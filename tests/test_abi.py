@@ -170,3 +170,109 @@ def test_no_gpu_valid_plan_reports_hip_error_not_crash():
     st, out, err = plan_status([desc(0)])
     assert st == -5 and out is None
     assert err.startswith("hip")
+
+
+# ---- TP shard apply: validation (every case fails before any HIP call)
+
+def shard(i, rows=64, cols=128, ldp=None, ldd=None):
+    stride = 1 << 24
+    b = BASE + (64 + i) * 2 * stride
+    return muon.muon_shard(b, b + stride, rows, cols, ldp or cols, ldd or cols)
+
+
+def apply_status(shards, dtype=muon.MUON_BF16, n=None):
+    arr = (muon.muon_shard * max(len(shards), 1))(*shards)
+    out = ctypes.c_void_p(123)
+    st = muon.lib().muon_apply_plan(arr, len(shards) if n is None else n, dtype, ctypes.byref(out))
+    return st, out.value, muon.last_error()
+
+
+def test_shard_struct_layout_matches_header():
+    assert ctypes.sizeof(muon.muon_shard) == 48
+
+
+@pytest.mark.parametrize("case,status,msg", [
+    ("n0", -1, "n must be"),
+    ("p_null", -1, "NULL"),
+    ("rows0", -1, "rows and cols"),
+    ("too_big", -1, "2^24"),
+    ("ldp_small", -1, "ldp and ldd"),
+    ("ldd_small", -1, "ldp and ldd"),
+    ("dtype_7", -4, "dtype"),
+    ("misaligned", -3, "aligned"),
+    ("p_over_p", -2, "overlaps"),
+    ("p_over_d", -2, "overlaps"),
+    ("p_is_d", -2, "overlaps"),
+    ("column_blocks_overlap", -2, "overlaps"),
+    ("other_stride_over_p", -2, "overlaps"),
+])
+def test_apply_plan_validation(case, status, msg):
+    s = [shard(0), shard(1)]
+    n, dtype = None, muon.MUON_BF16
+    if case == "n0":
+        n = 0
+    elif case == "p_null":
+        s[1].p = None
+    elif case == "rows0":
+        s[0].rows = 0
+    elif case == "too_big":
+        s[0].cols = (1 << 24) + 1
+        s[0].ldp = s[0].ldd = s[0].cols
+    elif case == "ldp_small":
+        s[0].ldp = 100
+    elif case == "ldd_small":
+        s[1].ldd = 127
+    elif case == "dtype_7":
+        dtype = 7
+    elif case == "misaligned":
+        s[0].d = s[0].d + 1
+    elif case == "p_over_p":
+        s[1].p = s[0].p + 2 * 64 * 3          # inside shard 0's rows
+    elif case == "p_over_d":
+        s[1].d = s[0].p + 256
+    elif case == "p_is_d":
+        s[0].d = s[0].p
+    elif case == "column_blocks_overlap":
+        # two column blocks of one 64 x 256 matrix: columns [0, 128) and [100, 228)
+        s[0].ldp = s[1].ldp = 256
+        s[1].p = s[0].p + 2 * 100
+    elif case == "other_stride_over_p":
+        s[1].p = s[0].p + 2 * 1300           # a view with another stride, inside shard 0's range
+        s[1].ldp = 200
+    st, out, err = apply_status(s, dtype, n)
+    assert st == status, err
+    assert msg in err
+    assert out is None
+
+
+def test_disjoint_views_do_not_alias():
+    """Column blocks of one matrix with its row stride, read-only views that
+    share elements, and row blocks back to back all pass validation."""
+    rows, cols, parts = 64, 256, 4
+    b = BASE + (1 << 30)
+    w = cols // parts
+    s = [muon.muon_shard(b + 2 * r * w, b + (1 << 26), rows, w, cols, cols) for r in range(parts)]
+    s.append(muon.muon_shard(b + (1 << 25), b + (1 << 26), rows, w, w, cols))   # d shared with the others
+    st, out, err = apply_status(s)
+    assert st in (0, -5, -6), err          # the next failure (if any) comes from HIP
+    if st == 0:
+        assert muon.lib().muon_apply_plan_destroy(out) == 0
+
+
+def test_apply_null_arguments():
+    L = muon.lib()
+    out = ctypes.c_void_p()
+    assert L.muon_apply_plan(None, 1, muon.MUON_BF16, ctypes.byref(out)) == -1
+    arr = (muon.muon_shard * 1)(shard(0))
+    assert L.muon_apply_plan(arr, 1, muon.MUON_BF16, None) == -1
+    assert L.muon_apply(None, None) == -1
+    assert L.muon_apply_plan_destroy(None) == 0
+
+
+def test_no_gpu_valid_apply_plan_reports_hip_error_not_crash():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    st, out, err = apply_status([shard(0)])
+    assert st == -5 and out is None
+    assert err.startswith("hip")

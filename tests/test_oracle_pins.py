@@ -334,3 +334,63 @@ def test_step_flops_brute_force_count(r, c):
             per_iter += 2 * m          # one entry of the symmetric square
     per_iter += 2 * m * m * n          # B X
     assert ref.step_flops(r, c, 5) == 5 * per_iter
+
+
+# ---- tensor-parallel local update
+
+@pytest.mark.parametrize("rows,cols,ranks", [(8, 12, 2), (7, 5, 3), (5, 16, 4), (3, 2, 3), (1, 9, 1)])
+@pytest.mark.parametrize("kind", ["column", "row"])
+def test_tp_shards_partition_the_weight(rows, cols, ranks, kind):
+    count = np.zeros((rows, cols), dtype=int)
+    sizes = []
+    for rs, cs in ref.tp_shard_ranges(rows, cols, ranks, kind):
+        count[rs, cs] += 1
+        sizes.append((rs.stop - rs.start) if kind == "column" else (cs.stop - cs.start))
+        # the split dimension is the output one (rows) for column-parallel
+        # layers and the input one (cols) for row-parallel layers
+        if kind == "column":
+            assert (cs.start, cs.stop) == (0, cols)
+        else:
+            assert (rs.start, rs.stop) == (0, rows)
+    assert (count == 1).all()
+    assert max(sizes) - min(sizes) <= 1 and sum(sizes) == (rows if kind == "column" else cols)
+
+
+@pytest.mark.parametrize("kind", ["column", "row"])
+def test_shard_updates_reassemble_the_whole_matrix_sum(kind):
+    rng = np.random.default_rng(7)
+    W = rng.standard_normal((6, 10))
+    dW = rng.standard_normal((6, 10))
+    out = np.full_like(W, np.nan)
+    for rs, cs in ref.tp_shard_ranges(6, 10, 4, kind):
+        out[rs, cs] = ref.apply_shard(W[rs, cs].copy(), dW[rs, cs])
+    for i in range(6):                       # brute force, element by element
+        for j in range(10):
+            assert out[i, j] == W[i, j] + dW[i, j]
+
+
+def _bf16_round_once(x):
+    """float64 -> the nearest bf16 value (ties to even), in one rounding."""
+    m, e = np.frexp(np.asarray(x, dtype=np.float64))
+    return np.ldexp(np.round(m * 256.0) / 256.0, e)
+
+
+def test_fp32_sum_then_bf16_store_is_the_exactly_rounded_sum():
+    """The shard kernel adds two bf16 values in fp32 and rounds the sum once to
+    bf16. That equals rounding the exact sum once: either the fp32 sum is exact
+    (exponents within 16 of each other), or the smaller term is far below half
+    a bf16 unit of the larger. Checked here on random pairs with every exponent
+    gap up to 30, signs mixed (cancellation included), and on halfway cases."""
+    from matrix_optimizer_step_muon_amd import workloads as wl
+    rng = np.random.default_rng(11)
+    n = 400_000
+    a = _bf16_round_once(rng.standard_normal(n) * np.exp2(rng.integers(-20, 20, n)))
+    gap = rng.integers(0, 31, n).astype(float)
+    b = _bf16_round_once(rng.standard_normal(n) * np.abs(a) * np.exp2(-gap))
+    # halfway cases: b = half a bf16 unit of a (and just above or below it)
+    ulp = np.exp2(np.frexp(a)[1] - 8)
+    b[:3000] = 0.5 * ulp[:3000]
+    b[3000:6000] = _bf16_round_once(0.5 * ulp[3000:6000] * (1 + 2.0 ** -7))
+    b[6000:9000] = _bf16_round_once(0.5 * ulp[6000:9000] * (1 - 2.0 ** -8))
+    fp32_then_bf16 = wl.bf16_bits_to_f32(wl.f32_to_bf16_bits(a.astype(np.float32) + b.astype(np.float32)))
+    assert np.array_equal(fp32_then_bf16.astype(np.float64), _bf16_round_once(a + b))
