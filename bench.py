@@ -63,6 +63,8 @@ def parse():
                     help="protocol runs after the timed region: each a fresh plan, 3 warm-up and "
                          "--run-steps timed steps (0: none)")
     ap.add_argument("--run-steps", type=int, default=10)
+    ap.add_argument("--no-master-weights", action="store_true",
+                    help="skip the step with fp32 master weights and momentum (MUON_BF16_F32_MASTER)")
     ap.add_argument("--no-tp-apply", action="store_true",
                     help="skip the measurement of the tensor-parallel local update (muon_apply)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -262,6 +264,39 @@ def tp_apply_measure(mu, shapes, dtype, stream, ranks=8, reps=20):
                     "matrices (column-parallel: row blocks; row-parallel: column blocks, strided views)"}
 
 
+def master_weights_measure(mu, wload, stream, steps, warmup, alg_flops):
+    """The same step with fp32 master weights and momentum and bf16 gradients
+    (MUON_BF16_F32_MASTER), on the same shapes: seeded synthetic fp32 W and M
+    and bf16 G, resident in HBM; `warmup` untimed and `steps` timed steps."""
+    import torch
+    dev = []
+    for i, (r, c) in enumerate(wload.shapes):
+        g = torch.Generator(device="cuda").manual_seed(1000 + i)
+        W = torch.randn(r, c, device="cuda", generator=g).mul_(wload.w_std)
+        G = torch.randn(r, c, device="cuda", generator=g).mul_(wload.g_std).to(torch.bfloat16)
+        M = torch.randn(r, c, device="cuda", generator=g).mul_(wload.g_std)
+        dev.append([W, G, M])
+    plan = mu.Plan(dev, **wload.hparams())
+    for _ in range(warmup):
+        plan.step(stream)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        plan.step(stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    plan.close()
+    del dev
+    return {"dtype": "W, M fp32; G bf16; Newton-Schulz bf16", "ms_per_step": round(ms, 4),
+            "value": round(alg_flops / (ms / 1e3) / 1e12, 2), "unit": "TFLOP/s",
+            "fraction_of_peak": round(alg_flops / (ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "elementwise_min_bytes_per_elem": 18,
+            "what": "the same shapes and step count; the elementwise minimum is 18 B per element "
+                    "(read G 2, M 4, W 4; write M' 4, W' 4) against 10 B in bf16"}
+
+
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "update_kernel_traffic_qwen3_32b_layer.txt")
 KERNEL_SOURCE = os.path.join(ROOT, "matrix_optimizer_step_muon_amd", "csrc", "muon_kernels.hip")
 
@@ -411,6 +446,12 @@ def main():
         print(f"[bench] protocol: {args.runs} runs x {args.run_steps} steps, mean {proto['mean_ms']:.3f} ms",
               file=sys.stderr, flush=True)
 
+    master = None
+    if wload.dtype == "bf16" and not args.no_master_weights:
+        master = master_weights_measure(mu, wload, stream, args.steps, args.warmup,
+                                        nsflops(wload.shapes, wload.ns_steps)["total"])
+        print(f"[bench] fp32 master weights: {master['ms_per_step']:.3f} ms per step", file=sys.stderr, flush=True)
+
     tp_apply = None
     if not args.no_tp_apply:
         tp_apply = tp_apply_measure(mu, wload.shapes, wload.dtype, stream)
@@ -481,6 +522,7 @@ def main():
             "avg_launch_ms": round(upd_avg, 4),
         },
         "kernels": per_kernel,
+        "master_weights": master,
         "tp_apply": tp_apply,
         "momentum_hbm": {"achieved_gbs": round(mom_gbs, 1) if mom_gbs else None,
                          "peak_gbs": HBM_PEAK_GBS, "alg_bytes_per_elem": 4 * elem},

@@ -23,7 +23,8 @@
  * - It returns muon_status (0 = MUON_OK) and never throws or aborts across the
  *   ABI. On error, muon_last_error() gives this thread's message.
  * - Pointers named w, g, m and delta are device pointers. They address
- *   row-major, contiguous matrices of one dtype.
+ *   row-major, contiguous matrices of the plan's dtype (MUON_BF16_F32_MASTER:
+ *   fp32 w, m and delta with a bf16 g).
  * - Every other pointer is a host pointer.
  */
 #ifndef MUON_H_
@@ -48,8 +49,14 @@ typedef enum {
 
 typedef enum {
   MUON_F32 = 0,  /* W, G, M fp32; all arithmetic fp32 (fp32 MFMA)          */
-  MUON_BF16 = 1  /* W, G, M bf16; bf16 MFMA with fp32 accumulation,         */
+  MUON_BF16 = 1, /* W, G, M bf16; bf16 MFMA with fp32 accumulation,         */
                  /* intermediates stored bf16 (round to nearest even)      */
+  MUON_BF16_F32_MASTER = 2
+                 /* fp32 master weights and momentum with bf16 gradients,  */
+                 /* the training setup of the pages (Canzona analysis page, */
+                 /* section 3.4, the Atomicity Constraint): W, M and delta  */
+                 /* fp32, G bf16; X, A and B bf16 as for MUON_BF16, and     */
+                 /* W' = W - lr*s*O formed in fp32 and stored fp32         */
 } muon_dtype;
 
 /* One matrix of the batch: rows x cols, row-major, contiguous.

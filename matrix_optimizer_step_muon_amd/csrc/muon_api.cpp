@@ -46,8 +46,9 @@ constexpr int32_t kMaxNsSteps = 1000;
 
 struct muon_plan_s {
   muon_hparams hp{};
-  int dtype = 1;
-  int elem = 2;
+  int dtype = 1;       // muon_dtype: the storage types of w, g, m, delta
+  int gemm_dtype = 1;  // the Newton-Schulz engine: 1 bf16, 0 fp32
+  int elem = 2;        // workspace element size (X, A, B)
   int n = 0;
   int device = 0;
   int tile = muon::kTileBF16;
@@ -134,9 +135,11 @@ muon_status validate(const muon_matrix* mats, int32_t n, const muon_hparams* hp)
   if (hp->ns_steps < 0 || hp->ns_steps > kMaxNsSteps)
     return fail(MUON_ERR_INVALID_ARG, "ns_steps must be in [0, 1000]");
   if (hp->nesterov != 0 && hp->nesterov != 1) return fail(MUON_ERR_INVALID_ARG, "nesterov must be 0 or 1");
-  if (hp->dtype != MUON_F32 && hp->dtype != MUON_BF16)
-    return fail(MUON_ERR_UNSUPPORTED, "dtype must be MUON_F32 or MUON_BF16");
-  const size_t elem = hp->dtype == MUON_BF16 ? 2 : 4;
+  if (hp->dtype != MUON_F32 && hp->dtype != MUON_BF16 && hp->dtype != MUON_BF16_F32_MASTER)
+    return fail(MUON_ERR_UNSUPPORTED, "dtype must be MUON_F32, MUON_BF16 or MUON_BF16_F32_MASTER");
+  // Element sizes of w, g, m and delta.
+  const size_t es[4] = {hp->dtype == MUON_BF16 ? 2u : 4u, hp->dtype == MUON_F32 ? 4u : 2u,
+                        hp->dtype == MUON_BF16 ? 2u : 4u, hp->dtype == MUON_BF16 ? 2u : 4u};
 
   struct Range { uintptr_t lo, hi; int mat; const char* what; };
   std::vector<Range> ranges;
@@ -150,14 +153,13 @@ muon_status validate(const muon_matrix* mats, int32_t n, const muon_hparams* hp)
     if (!d.g) return fail(MUON_ERR_INVALID_ARG, at + "g is NULL");
     if (!d.m) return fail(MUON_ERR_INVALID_ARG, at + "m is NULL");
     if (!d.w && !d.delta) return fail(MUON_ERR_INVALID_ARG, at + "w and delta are both NULL");
-    const uintptr_t bytes = uintptr_t(d.rows) * uintptr_t(d.cols) * elem;
     const void* ptrs[4] = {d.w, d.g, d.m, d.delta};
     const char* what[4] = {"w", "g", "m", "delta"};
     for (int k = 0; k < 4; ++k) {
       if (!ptrs[k]) continue;
       const uintptr_t p = reinterpret_cast<uintptr_t>(ptrs[k]);
       if (p % 16 != 0) return fail(MUON_ERR_ALIGN, at + what[k] + " is not 16-byte aligned");
-      ranges.push_back({p, p + bytes, i, what[k]});
+      ranges.push_back({p, p + uintptr_t(d.rows) * uintptr_t(d.cols) * es[k], i, what[k]});
     }
   }
   std::sort(ranges.begin(), ranges.end(), [](const Range& x, const Range& y) { return x.lo < y.lo; });
@@ -193,9 +195,11 @@ muon_status muon_plan(const muon_matrix* mats, int32_t n, const muon_hparams* hp
   auto* p = new muon_plan_s();
   p->hp = *hp;
   p->dtype = hp->dtype;
-  p->elem = hp->dtype == MUON_BF16 ? 2 : 4;
+  // Newton-Schulz runs in bf16 for MUON_BF16 and MUON_BF16_F32_MASTER.
+  p->gemm_dtype = hp->dtype == MUON_F32 ? 0 : 1;
+  p->elem = p->gemm_dtype == 1 ? 2 : 4;
   p->n = n;
-  p->tile = hp->dtype == MUON_BF16 ? muon::kTileBF16 : muon::kTileF32;
+  p->tile = p->gemm_dtype == 1 ? muon::kTileBF16 : muon::kTileF32;
   const int64_t T = p->tile;
 
   // MUON_GEMM_VARIANT=0|1|2|3 picks the bf16 engine pipeline (a tuning knob;
@@ -207,7 +211,12 @@ muon_status muon_plan(const muon_matrix* mats, int32_t n, const muon_hparams* hp
   // Chains: two for the bf16 four-wave engines (MUON_CHAINS=C overrides, C in
   // [1, 8]), one otherwise; never more than there are matrices. Matrices go
   // largest first (multiply-adds of one iteration) to the lightest chain.
-  int C = (p->dtype == 1 && (p->variant == muon::kGemm4W || p->variant == muon::kGemm4WDeep)) ? 2 : 1;
+  const bool four_wave = p->variant == muon::kGemm4W || p->variant == muon::kGemm4WDeep;
+  if (p->dtype == MUON_BF16_F32_MASTER && !four_wave) {
+    free_plan(p);
+    return fail(MUON_ERR_UNSUPPORTED, "MUON_BF16_F32_MASTER needs the four-wave GEMM engine (MUON_GEMM_VARIANT 2 or 3)");
+  }
+  int C = (p->gemm_dtype == 1 && four_wave) ? 2 : 1;
   if (const char* v = std::getenv("MUON_CHAINS")) C = std::max(1, std::min(8, std::atoi(v)));
   C = std::min<int>(C, n);
   std::vector<std::vector<int32_t>> members(C);
@@ -376,7 +385,7 @@ muon_status muon_plan(const muon_matrix* mats, int32_t n, const muon_hparams* hp
   int n_cu = 0;
   e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, p->device);
   if (e != hipSuccess) { free_plan(p); return hip_fail(e, "hipDeviceGetAttribute"); }
-  const int32_t resident = n_cu * muon::gemm_blocks_per_cu(p->dtype, p->variant);
+  const int32_t resident = n_cu * muon::gemm_blocks_per_cu(p->gemm_dtype, p->variant);
   for (auto& ch : p->chains)
     for (int ph = 0; ph < 3; ++ph) ch.grid[ph] = std::max(1, std::min(ch.n_tiles[ph], resident));
   // Auxiliary streams (default priority, not synchronising with the null
@@ -580,9 +589,9 @@ muon_status muon_step(muon_plan_t p, void* stream) {
         hipStream_t q = c == 0 ? s : p->aux[c - 1];
         muon::PhaseArgs a{p->d_mats, ch.d_tiles[ph], ch.d_qoff + ph * (muon::kQueues + 1),
                           p->d_counters + ((c * T + it) * 3 + ph) * muon::kQueues, p->d_scale, it & 1, it == 0,
-                          it == T - 1, co};
+                          it == T - 1, p->dtype == MUON_BF16_F32_MASTER ? 1 : 0, co};
         run_on(q, MUON_K_GRAM + ph,
-               [&] { return muon::launch_phase(p->dtype, p->variant, muon::Phase(ph), a, ch.grid[ph], q); });
+               [&] { return muon::launch_phase(p->gemm_dtype, p->variant, muon::Phase(ph), a, ch.grid[ph], q); });
       }
     }
   }

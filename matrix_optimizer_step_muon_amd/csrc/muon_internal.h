@@ -73,6 +73,7 @@ struct PhaseArgs {
   int32_t src;         // ping/pong index read this iteration
   int32_t first;       // first iteration: fold the norm scale in
   int32_t last;        // last iteration: apply to W / delta instead of storing X
+  int32_t wf32;        // W and delta are fp32 (fp32 master weights), X, A, B bf16
   StepCoeffs co;
 };
 

@@ -1543,31 +1543,61 @@ MUON_INLINE void mirror_out(const unsigned char* epi, u16* dst_t, int64_t ld_t, 
   }
 }
 
-// Last iteration, staged half H of the X tile (tile rows half_row(r, H)).
-// Wide matrix: W rows tr + half_row(r, H), read by rows; tall matrix (X = the
-// transposed update): those W columns of W rows tc + c, read by columns. A thread's 16 runs of 8 are applied in one batch: all W loads are
-// in flight together, so the half costs one memory round trip, not 16.
 // What the last iteration's apply needs of a matrix, as scalars.
 struct ApplyDev {
-  u16* w;
-  u16* delta;
+  void* w;      // W, of the apply's storage type (bf16 or fp32), or null
+  void* delta;  // delta, of the same type, or null
   float ls;
   int64_t rows, cols;
   int tall;
 };
 
-template <int NT>
+// Element e (0..7) of an 8-element W run loaded as NV 16-byte vectors.
+template <class TW>
+MUON_INLINE float w_elem(const u32x4 (&v)[sizeof(TW) / 2], int e) {
+  if constexpr (sizeof(TW) == 2) return __uint_as_float(e & 1 ? v[0][e >> 1] & 0xffff0000u : v[0][e >> 1] << 16);
+  else return __uint_as_float(v[e >> 2][e & 3]);
+}
+
+// Stores 8 values as one 8-element run of TW (16 bytes of bf16, 32 of fp32).
+template <class TW>
+MUON_INLINE void w_store8(TW* p, const float (&x)[8]) {
+  if constexpr (sizeof(TW) == 2) {
+    u32x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = pack_bf16x2(x[2 * e], x[2 * e + 1]);
+    *((g_u32x4*)(p)) = v;
+  } else {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      f32x4 v = {x[4 * k], x[4 * k + 1], x[4 * k + 2], x[4 * k + 3]};
+      *((g_f32x4*)(p + 4 * k)) = v;
+    }
+  }
+}
+
+// Last iteration, staged half H of the X tile (tile rows half_row(r, H)).
+// Wide matrix: W rows tr + half_row(r, H), read by rows; tall matrix (X = the
+// transposed update): those W columns of W rows tc + c, read by columns. A
+// thread's 16 runs of 8 are applied in batches whose W loads are all in flight
+// together, so a batch costs one memory round trip, not one per run: one batch
+// for bf16 W, two for fp32 W.
+template <int NT, class TW>
 MUON_INLINE void apply_half(const unsigned char* epi, const ApplyDev& d, int64_t tr, int64_t tc, int H) {
   constexpr int N = kEpiRows * 32 / NT;
   constexpr int NW = NT / 64;
   static_assert(N == 64 / NW, "row and column item counts agree");
+  // W runs of 8 elements: one 16-byte vector for bf16, two for fp32, which
+  // take twice the registers per run, hence the second batch.
+  constexpr int NV = sizeof(TW) / 2;
+  constexpr int B = N / NV;
   const int64_t R = d.rows, C = d.cols;
-  u16* W = d.w;
-  u16* D = d.delta;
+  TW* W = static_cast<TW*>(d.w);
+  TW* D = static_cast<TW*>(d.delta);
   const float ls = d.ls;
   const int tid = fresh_tid();
   const int wave = tid >> 6, G = (tid >> 4) & 3, i = tid & 15;
-  u32x4 ov[N], wv[N];
+  u32x4 ov[N];
   int64_t gr[N], gc[N];
 #pragma unroll
   for (int p = 0; p < N; ++p) {
@@ -1584,50 +1614,58 @@ MUON_INLINE void apply_half(const unsigned char* epi, const ApplyDev& d, int64_t
       ov[p] = stage_read_col8(epi, r0, c0, tid);  // every lane takes part
     }
   }
-  // Whole aligned runs: W loaded for all items first.
 #pragma unroll
-  for (int p = 0; p < N; ++p) {
-    const int64_t base = gr[p] * C + gc[p];
-    const bool fast = gr[p] < R && gc[p] + 8 <= C && (base & 7) == 0;
-    wv[p] = u32x4{0u, 0u, 0u, 0u};
-    if (W && fast) wv[p] = *((const g_u32x4*)(W + base));
-  }
+  for (int b0 = 0; b0 < N; b0 += B) {
+    // Whole aligned runs: W loaded for all items of the batch first.
+    u32x4 wv[B][NV];
 #pragma unroll
-  for (int p = 0; p < N; ++p) {
-    if (gr[p] >= R || gc[p] >= C) continue;
-    const int64_t base = gr[p] * C + gc[p];
-    if (gc[p] + 8 <= C && (base & 7) == 0) {
-      float o[8];
+    for (int q = 0; q < B; ++q) {
+      const int p = b0 + q;
+      const int64_t base = gr[p] * C + gc[p];
+      const bool fast = gr[p] < R && gc[p] + 8 <= C && (base & 7) == 0;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        o[2 * e] = __uint_as_float(ov[p][e] << 16);
-        o[2 * e + 1] = __uint_as_float(ov[p][e] & 0xffff0000u);
+      for (int k = 0; k < NV; ++k) {
+        wv[q][k] = u32x4{0u, 0u, 0u, 0u};
+        if (W && fast) wv[q][k] = *((const g_u32x4*)(W + base) + k);
       }
-      if (W) {
-        u32x4 nv;
+    }
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          nv[e] = pack_bf16x2(__uint_as_float(wv[p][e] << 16) - ls * o[2 * e],
-                              __uint_as_float(wv[p][e] & 0xffff0000u) - ls * o[2 * e + 1]);
-        *((g_u32x4*)(W + base)) = nv;
-      }
-      if (D) {
-        u32x4 dv;
+    for (int q = 0; q < B; ++q) {
+      const int p = b0 + q;
+      if (gr[p] >= R || gc[p] >= C) continue;
+      const int64_t base = gr[p] * C + gc[p];
+      if (gc[p] + 8 <= C && (base & 7) == 0) {
+        float o[8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dv[e] = pack_bf16x2(-ls * o[2 * e], -ls * o[2 * e + 1]);
-        *((g_u32x4*)(D + base)) = dv;
-      }
-    } else {  // ragged edge or unaligned row: element by element
-      for (int e = 0; e < 8 && gc[p] + e < C; ++e) {
-        const float o = __uint_as_float(e & 1 ? ov[p][e >> 1] & 0xffff0000u : ov[p][e >> 1] << 16);
-        if (W) Elem<u16>::store(W + base + e, Elem<u16>::load(W + base + e) - ls * o);
-        if (D) Elem<u16>::store(D + base + e, -ls * o);
+        for (int e = 0; e < 4; ++e) {
+          o[2 * e] = __uint_as_float(ov[p][e] << 16);
+          o[2 * e + 1] = __uint_as_float(ov[p][e] & 0xffff0000u);
+        }
+        if (W) {
+          float nw[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) nw[e] = w_elem<TW>(wv[q], e) - ls * o[e];
+          w_store8(W + base, nw);
+        }
+        if (D) {
+          float nd[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) nd[e] = -ls * o[e];
+          w_store8(D + base, nd);
+        }
+      } else {  // ragged edge or unaligned row: element by element
+        for (int e = 0; e < 8 && gc[p] + e < C; ++e) {
+          const float o = __uint_as_float(e & 1 ? ov[p][e >> 1] & 0xffff0000u : ov[p][e >> 1] << 16);
+          if (W) Elem<TW>::store(W + base + e, Elem<TW>::load(W + base + e) - ls * o);
+          if (D) Elem<TW>::store(D + base + e, -ls * o);
+        }
       }
     }
   }
 }
 
-template <class E, int PH>
+// WF32: W and delta are fp32 (fp32 master weights; the last update only).
+template <class E, int PH, bool WF32 = false>
 __global__ void __launch_bounds__(E::NT) phase_kernel4(PhaseArgs args) {
   static_assert(E::LDS_BYTES + kEpiExtra <= 160 * 1024, "ring + staging exceed LDS");
   static_assert(E::STAGE_BYTES >= kEpiBytes - kEpiExtra, "the staging half must not reach the preloaded stages");
@@ -1768,8 +1806,9 @@ __global__ void __launch_bounds__(E::NT) phase_kernel4(PhaseArgs args) {
         } else {
           stage_half<E, H>(acc, epi, us);
           __syncthreads();
-          const ApplyDev ad{static_cast<u16*>(d.w), static_cast<u16*>(d.delta), d.lr_scale, d.rows, d.cols, d.tall};
-          apply_half<E::NT>(epi, ad, tr, tc, H);
+          const ApplyDev ad{d.w, d.delta, d.lr_scale, d.rows, d.cols, d.tall};
+          if constexpr (WF32) apply_half<E::NT, float>(epi, ad, tr, tc, H);
+          else apply_half<E::NT, u16>(epi, ad, tr, tc, H);
         }
       };
       half(std::integral_constant<int, 0>{});
@@ -1811,11 +1850,13 @@ MUON_INLINE float block_sum_256(float v, float* red) {
 }
 
 // Fused momentum. One 64 x 64 tile of one matrix per workgroup of 256 threads.
-// Nothing here mixes elements of a tile, except the sum of squares.
-template <class T>
+// Nothing here mixes elements of a tile, except the sum of squares. TG, TM
+// and TX are the storage types of G, of M and of the X buffer (all bf16, all
+// fp32, or bf16 G and X with an fp32 M).
+template <class TG, class TM, class TX>
 __global__ void __launch_bounds__(256) momentum_kernel(EwArgs args) {
   constexpr int TS = kEwTile;
-  __shared__ T tileU[TS][TS + (sizeof(T) == 2 ? 2 : 1)];
+  __shared__ TX tileU[TS][TS + (sizeof(TX) == 2 ? 2 : 1)];
   __shared__ float red[4];
   const int tid = threadIdx.x;
   if (blockIdx.x == 0)
@@ -1827,11 +1868,11 @@ __global__ void __launch_bounds__(256) momentum_kernel(EwArgs args) {
   const int64_t r0 = (int64_t)(local / d.ew_tiles_c) * TS;
   const int64_t c0 = (int64_t)(local % d.ew_tiles_c) * TS;
   const int rows = d.rows, cols = d.cols;
-  const T* G = static_cast<const T*>(d.g);
-  T* Mo = static_cast<T*>(d.mom);
+  const TG* G = static_cast<const TG*>(d.g);
+  TM* Mo = static_cast<TM*>(d.mom);
   // X0 = U (rows <= cols) or U^T (tall), in the X buffer: a wide matrix is
   // stored directly, a tall one through the LDS tile, transposed.
-  T* Xb = static_cast<T*>(d.x[0]);
+  TX* Xb = static_cast<TX*>(d.x[0]);
   const int64_t ldx = d.ldx;
   const bool tall = d.tall != 0;
   const float beta = args.co.beta;
@@ -1848,24 +1889,24 @@ __global__ void __launch_bounds__(256) momentum_kernel(EwArgs args) {
       const int64_t o = gr * cols + gc;
       if (vec_ok && gc + 3 < cols) {
         float g[4], mm[4], mn[4];
-        Vec4<T>::load(G + o, g);
-        Vec4<T>::load(Mo + o, mm);
+        Vec4<TG>::load(G + o, g);
+        Vec4<TM>::load(Mo + o, mm);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           mn[e] = beta * mm[e] + g[e];
           u[e] = nesterov ? g[e] + beta * mn[e] : mn[e];
         }
-        Vec4<T>::store(Mo + o, mn);
-        if (!tall) Vec4<T>::store(Xb + gr * ldx + gc, u);
+        Vec4<TM>::store(Mo + o, mn);
+        if (!tall) Vec4<TX>::store(Xb + gr * ldx + gc, u);
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           if (gc + e < cols) {
-            const float g = Elem<T>::load(G + o + e);
-            const float mn = beta * Elem<T>::load(Mo + o + e) + g;
+            const float g = Elem<TG>::load(G + o + e);
+            const float mn = beta * Elem<TM>::load(Mo + o + e) + g;
             u[e] = nesterov ? g + beta * mn : mn;
-            Elem<T>::store(Mo + o + e, mn);
-            if (!tall) Elem<T>::store(Xb + gr * ldx + gc + e, u[e]);
+            Elem<TM>::store(Mo + o + e, mn);
+            if (!tall) Elem<TX>::store(Xb + gr * ldx + gc + e, u[e]);
           }
         }
       }
@@ -1873,7 +1914,7 @@ __global__ void __launch_bounds__(256) momentum_kernel(EwArgs args) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       ss += u[e] * u[e];
-      tileU[lr][lc + e] = Elem<T>::to_storage(u[e]);
+      tileU[lr][lc + e] = Elem<TX>::to_storage(u[e]);
     }
   }
   const float tot = block_sum_256(ss, red);  // contains a barrier: tileU is complete
@@ -1886,14 +1927,14 @@ __global__ void __launch_bounds__(256) momentum_kernel(EwArgs args) {
     const int lc = p * 16 + (tid >> 4), lr = (tid & 15) * 4;
     const int64_t gc = c0 + lc, gr = r0 + lr;
     if (gc >= cols) continue;
-    T* dst = Xb + gc * ldx + gr;
+    TX* dst = Xb + gc * ldx + gr;
     if (gr + 3 < rows) {
       float v[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = Elem<T>::lds_load(&tileU[lr + e][lc]);
-      Vec4<T>::store(dst, v);
+      for (int e = 0; e < 4; ++e) v[e] = Elem<TX>::lds_load(&tileU[lr + e][lc]);
+      Vec4<TX>::store(dst, v);
     } else {
-      for (int e = 0; e < 4 && gr + e < rows; ++e) Elem<T>::store(dst + e, Elem<T>::lds_load(&tileU[lr + e][lc]));
+      for (int e = 0; e < 4 && gr + e < rows; ++e) Elem<TX>::store(dst + e, Elem<TX>::lds_load(&tileU[lr + e][lc]));
     }
   }
 }
@@ -1915,25 +1956,26 @@ __global__ void __launch_bounds__(256) norm_kernel(const MatDev* mats, const flo
   if (threadIdx.x == 0) scale[blockIdx.x] = (float)(1.0 / (sqrt(red[0]) + (double)eps));
 }
 
-// T = 0: O = s*U, so W -= lr*scale*s*U and delta = -lr*scale*s*U.
-template <class T>
+// T = 0: O = s*U, so W -= lr*scale*s*U and delta = -lr*scale*s*U. TX is the
+// X buffer's storage type, TW that of W and delta.
+template <class TX, class TW>
 __global__ void __launch_bounds__(256) apply_kernel(EwArgs args) {
   const int mi = find_mat(args.prefix, args.n_mats, blockIdx.x);
   const MatDev& d = args.mats[mi];
   const int local = blockIdx.x - args.prefix[mi];
   const int64_t r0 = (int64_t)(local / d.ew_tiles_c) * kEwTile;
   const int64_t c0 = (int64_t)(local % d.ew_tiles_c) * kEwTile;
-  const T* Xb = static_cast<const T*>(d.x[0]);  // U, or U^T for a tall matrix
-  T* W = static_cast<T*>(d.w);
-  T* D = static_cast<T*>(d.delta);
+  const TX* Xb = static_cast<const TX*>(d.x[0]);  // U, or U^T for a tall matrix
+  TW* W = static_cast<TW*>(d.w);
+  TW* D = static_cast<TW*>(d.delta);
   const float f = d.lr_scale * args.scale[mi];
   for (int e = threadIdx.x; e < kEwTile * kEwTile; e += 256) {
     const int64_t gr = r0 + e / kEwTile, gc = c0 + e % kEwTile;
     if (gr >= d.rows || gc >= d.cols) continue;
-    const float o = f * Elem<T>::load(Xb + (d.tall ? gc * d.ldx + gr : gr * d.ldx + gc));
+    const float o = f * Elem<TX>::load(Xb + (d.tall ? gc * d.ldx + gr : gr * d.ldx + gc));
     const int64_t wo = gr * d.cols + gc;
-    if (W) Elem<T>::store(W + wo, Elem<T>::load(W + wo) - o);
-    if (D) Elem<T>::store(D + wo, -o);
+    if (W) Elem<TW>::store(W + wo, Elem<TW>::load(W + wo) - o);
+    if (D) Elem<TW>::store(D + wo, -o);
   }
 }
 
@@ -1977,8 +2019,9 @@ __global__ void __launch_bounds__(256) shard_apply_kernel(const ShardDev* shards
 // ------------------------------------------------------------ launchers
 
 hipError_t launch_momentum(int dtype, const EwArgs& args, int32_t n_blocks, hipStream_t s) {
-  if (dtype == 1) hipLaunchKernelGGL(momentum_kernel<u16>, dim3(n_blocks), dim3(256), 0, s, args);
-  else hipLaunchKernelGGL(momentum_kernel<float>, dim3(n_blocks), dim3(256), 0, s, args);
+  if (dtype == 1) hipLaunchKernelGGL((momentum_kernel<u16, u16, u16>), dim3(n_blocks), dim3(256), 0, s, args);
+  else if (dtype == 2) hipLaunchKernelGGL((momentum_kernel<u16, float, u16>), dim3(n_blocks), dim3(256), 0, s, args);
+  else hipLaunchKernelGGL((momentum_kernel<float, float, float>), dim3(n_blocks), dim3(256), 0, s, args);
   return hipGetLastError();
 }
 
@@ -1996,8 +2039,9 @@ hipError_t launch_shard_apply(int dtype, const ShardDev* shards, const int32_t* 
 }
 
 hipError_t launch_apply(int dtype, const EwArgs& args, int32_t n_blocks, hipStream_t s) {
-  if (dtype == 1) hipLaunchKernelGGL(apply_kernel<u16>, dim3(n_blocks), dim3(256), 0, s, args);
-  else hipLaunchKernelGGL(apply_kernel<float>, dim3(n_blocks), dim3(256), 0, s, args);
+  if (dtype == 1) hipLaunchKernelGGL((apply_kernel<u16, u16>), dim3(n_blocks), dim3(256), 0, s, args);
+  else if (dtype == 2) hipLaunchKernelGGL((apply_kernel<u16, float>), dim3(n_blocks), dim3(256), 0, s, args);
+  else hipLaunchKernelGGL((apply_kernel<float, float>), dim3(n_blocks), dim3(256), 0, s, args);
   return hipGetLastError();
 }
 
@@ -2023,7 +2067,9 @@ static hipError_t launch_phase_e4(Phase ph, const PhaseArgs& args, int32_t grid,
     case kGram: hipLaunchKernelGGL((phase_kernel4<E, kGram>), dim3(grid), dim3(E::NT), 0, s, args); break;
     case kSquare: hipLaunchKernelGGL((phase_kernel4<E, kSquare>), dim3(grid), dim3(E::NT), 0, s, args); break;
     default:
-      if (args.last) hipLaunchKernelGGL((phase_kernel4<EQ, kUpdateLast>), dim3(grid), dim3(EQ::NT), 0, s, args);
+      if (args.last && args.wf32)
+        hipLaunchKernelGGL((phase_kernel4<EQ, kUpdateLast, true>), dim3(grid), dim3(EQ::NT), 0, s, args);
+      else if (args.last) hipLaunchKernelGGL((phase_kernel4<EQ, kUpdateLast>), dim3(grid), dim3(EQ::NT), 0, s, args);
       else hipLaunchKernelGGL((phase_kernel4<EQ, kUpdate>), dim3(grid), dim3(EQ::NT), 0, s, args);
       break;
   }

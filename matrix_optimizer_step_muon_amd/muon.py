@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(PKG, "_lib", "libmuon.so")
 MUON_OK = 0
 STATUS_NAMES = {0: "OK", -1: "INVALID_ARG", -2: "ALIAS", -3: "ALIGN", -4: "UNSUPPORTED",
                 -5: "HIP", -6: "OOM"}
-MUON_F32, MUON_BF16 = 0, 1
+MUON_F32, MUON_BF16, MUON_BF16_F32_MASTER = 0, 1, 2
 KERNEL_KINDS = ("momentum", "norm", "gram", "square", "update", "apply")
 MUON_K_COUNT = len(KERNEL_KINDS)
 
@@ -132,11 +132,25 @@ def _dtype_code(t) -> int:
     raise MuonError(-4, f"unsupported tensor dtype {t.dtype}")
 
 
+def _batch_dtype(W, G, M, D) -> int:
+    """The plan dtype of one matrix's tensors: all bf16, all fp32, or fp32 W,
+    M and delta with a bf16 G (fp32 master weights)."""
+    import torch
+    codes = {_dtype_code(t) for t in (W, M, D) if t is not None}
+    g = _dtype_code(G)
+    if codes == {g}:
+        return g
+    if codes == {MUON_F32} and g == MUON_BF16:
+        return MUON_BF16_F32_MASTER
+    raise MuonError(-1, "W, M and delta must share G's dtype, or be fp32 with a bf16 G")
+
+
 class Plan:
     """A static plan over a batch of ``(W, G, M[, delta])`` device tensors.
 
-    Tensors must be 2-D, contiguous, on one GPU, all bf16 or all fp32. They stay
-    referenced by the plan, since it keeps their addresses.
+    Tensors must be 2-D, contiguous and on one GPU: all bf16, all fp32, or fp32
+    W, M and delta with a bf16 G (fp32 master weights), the same for every
+    matrix. They stay referenced by the plan, since it keeps their addresses.
     """
 
     def __init__(self, mats: Iterable[Sequence], *, lr=0.02, beta=0.95, eps=1e-7,
@@ -149,15 +163,17 @@ class Plan:
             W, G, M = entry[0], entry[1], entry[2]
             D = entry[3] if len(entry) > 3 else None
             ref = W if W is not None else D
-            code = _dtype_code(ref)
-            dtype = code if dtype is None else dtype
             for t in (W, G, M, D):
                 if t is None:
                     continue
                 if not t.is_cuda or not t.is_contiguous() or t.dim() != 2:
                     raise MuonError(-1, "tensors must be contiguous 2-D device tensors")
-                if _dtype_code(t) != dtype or tuple(t.shape) != tuple(ref.shape):
-                    raise MuonError(-1, "tensors of a batch must share one dtype and shape per matrix")
+                if tuple(t.shape) != tuple(ref.shape):
+                    raise MuonError(-1, "the tensors of a matrix must share one shape")
+            code = _batch_dtype(W, G, M, D)
+            if dtype is not None and code != dtype:
+                raise MuonError(-1, "every matrix of a batch must have the same dtypes")
+            dtype = code
             self._tensors.append((W, G, M, D))
             descs.append(muon_matrix(W.data_ptr() if W is not None else None, G.data_ptr(),
                                      M.data_ptr(), D.data_ptr() if D is not None else None,

@@ -276,3 +276,33 @@ def test_no_gpu_valid_apply_plan_reports_hip_error_not_crash():
     st, out, err = apply_status([shard(0)])
     assert st == -5 and out is None
     assert err.startswith("hip")
+
+
+# ---- fp32 master weights (MUON_BF16_F32_MASTER): validation with per-pointer sizes
+
+def test_master_weights_ranges_use_fp32_sizes():
+    """w, m and delta are fp32 and g bf16: a g placed right after half of an
+    fp32 w overlaps it (it would not with a bf16 w)."""
+    rows, cols = 64, 128
+    b = BASE + (1 << 31)
+    nb16 = rows * cols * 2
+    hp = muon.make_hparams(dtype=muon.MUON_BF16_F32_MASTER)
+    d = muon.muon_matrix(b, b + nb16, b + 8 * nb16, None, rows, cols)
+    st, out, err = plan_status([d], hp)
+    assert st == -2 and "overlaps" in err, err
+    st_bf16, out_bf16, err_bf16 = plan_status([d], muon.make_hparams(dtype=muon.MUON_BF16))
+    assert st_bf16 in (0, -5, -6), err_bf16       # back to back in bf16: no alias
+    if st_bf16 == 0:
+        muon.destroy_raw(out_bf16)
+    d_ok = muon.muon_matrix(b, b + 2 * nb16, b + 3 * nb16, b + 5 * nb16, rows, cols)
+    st, out, err = plan_status([d_ok], hp)
+    assert st in (0, -5, -6), err
+    if st == 0:
+        muon.destroy_raw(out)
+
+
+def test_master_weights_need_the_four_wave_engine(monkeypatch):
+    monkeypatch.setenv("MUON_GEMM_VARIANT", "0")
+    hp = muon.make_hparams(dtype=muon.MUON_BF16_F32_MASTER)
+    st, out, err = plan_status([desc(0, elem=4)], hp)
+    assert st == -4 and "four-wave" in err and out is None
