@@ -23,10 +23,10 @@ Readings where the pages leave a step open:
 * the cut for rank r is searched among the boundaries at or after rank r-1's
   cut, and a tie in |Phi(u) - C| goes to the earlier boundary;
 * buckets of equal load keep their original order in the LPT order;
-* the Start_Index rule numbers ranks from 0: rank floor(start / S), with S the
-  bucket's size divided by R (the pages' worked example: a start of 1,048,577
-  with S = 1,048,576 falls in rank 1's slice), and the last rank takes any
-  start at or beyond (R - 1) S.
+* the Start_Index rule numbers ranks from 0 (the pages' worked example: a
+  start of 1,048,577 with S = 1,048,576 falls in rank 1's slice). With
+  S = |B| / R, r S <= start < (r + 1) S is start * R // |B| == r, which is
+  evaluated in integers, exactly.
 
 Every computation is a plain loop in float64 (integer sizes, float loads).
 """
@@ -47,18 +47,18 @@ def prefix_loads(loads: Sequence[float]) -> List[float]:
 def static_partition(sizes: Sequence[Sequence[int]], ranks: int) -> List[List[int]]:
     """Cuts of every bucket by the Start_Index rule (no load balancing).
 
-    Parameter p of bucket i goes to rank min(R - 1, floor(start(p) / S_i)),
-    S_i = |B_i| / R, start(p) = the number of elements before p in the bucket.
+    Parameter p of bucket i goes to rank floor(start(p) * R / |B_i|), i.e. the
+    r with r S_i <= start(p) < (r + 1) S_i for S_i = |B_i| / R, where start(p)
+    is the number of elements before p in the bucket.
     Returns, per bucket, the R + 1 cut indices (rank r owns parameters
     cuts[r] .. cuts[r+1] - 1)."""
     out = []
     for bucket in sizes:
         total = sum(bucket)
-        stride = total / ranks
         owner = []
         start = 0
         for n in bucket:
-            owner.append(min(ranks - 1, int(start // stride)))
+            owner.append(start * ranks // total)
             start += n
         cuts = [0] * (ranks + 1)
         for r in range(ranks + 1):
