@@ -297,6 +297,33 @@ def master_weights_measure(mu, wload, stream, steps, warmup, alg_flops):
                     "(read G 2, M 4, W 4; write M' 4, W' 4) against 10 B in bf16"}
 
 
+def dp_partition_measure(mu, wl, ranks=32, tp=8):
+    """The DP static partition (host) of a Qwen3-32B-shaped buffer: one TP
+    rank's local parameters in buckets, over `ranks` DP ranks, by the
+    Start_Index rule and by the alpha-Balanced Greedy LPT algorithm (alpha = 1,
+    loads = element counts). Reports R_LB = max/avg over ranks of the memory
+    (elements) and of the Muon FLOPs per step, and the planner's time."""
+    import math
+    buckets = wl.qwen3_32b_param_buffer(tp=tp)
+    sizes = [[math.prod(p) for p in b] for b in buckets]
+    flops = [[nsflops([p], 5)["total"] if len(p) == 2 else math.prod(p) for p in b] for b in buckets]
+    def r_lb(cuts, loads):
+        tot = [0.0] * ranks
+        for b, c in zip(loads, cuts):
+            for r in range(ranks):
+                tot[r] += sum(b[c[r]:c[r + 1]])
+        return round(max(tot) / (sum(tot) / ranks), 3)
+    out = {"buffer": f"Qwen3-32B-shaped, TP={tp} local shards, buckets of >= 40M elements",
+           "buckets": len(buckets), "params": sum(len(b) for b in buckets), "dp_ranks": ranks}
+    mu.dp_partition(sizes, ranks, alpha=1.0)   # first call: loads the library
+    for name, alpha in (("static", None), ("alpha_balanced", 1.0)):
+        t0 = time.perf_counter()
+        cuts, _ = mu.dp_partition(sizes, ranks, alpha=alpha)
+        ms = (time.perf_counter() - t0) * 1e3
+        out[name] = {"R_LB_memory": r_lb(cuts, sizes), "R_LB_flops": r_lb(cuts, flops), "ms": round(ms, 3)}
+    return out
+
+
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "update_kernel_traffic_qwen3_32b_layer.txt")
 KERNEL_SOURCE = os.path.join(ROOT, "matrix_optimizer_step_muon_amd", "csrc", "muon_kernels.hip")
 
@@ -452,6 +479,8 @@ def main():
                                         nsflops(wload.shapes, wload.ns_steps)["total"])
         print(f"[bench] fp32 master weights: {master['ms_per_step']:.3f} ms per step", file=sys.stderr, flush=True)
 
+    dp_part = dp_partition_measure(mu, wl)
+
     tp_apply = None
     if not args.no_tp_apply:
         tp_apply = tp_apply_measure(mu, wload.shapes, wload.dtype, stream)
@@ -523,6 +552,7 @@ def main():
         },
         "kernels": per_kernel,
         "master_weights": master,
+        "dp_partition": dp_part,
         "tp_apply": tp_apply,
         "momentum_hbm": {"achieved_gbs": round(mom_gbs, 1) if mom_gbs else None,
                          "peak_gbs": HBM_PEAK_GBS, "alg_bytes_per_elem": 4 * elem},

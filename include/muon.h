@@ -216,6 +216,39 @@ muon_status muon_apply(muon_apply_plan_t plan, void* stream);
 /* Frees the plan. NULL is a no-op. Synchronises the device. */
 muon_status muon_apply_plan_destroy(muon_apply_plan_t plan);
 
+/* ---------------------------------------------------------------------------
+ * Data-parallel static partition: which whole parameters each DP rank owns
+ * (host only, no GPU). A rank's share is the batch it passes to muon_plan.
+ *
+ * The parameter buffer is a list of n_buckets buckets; bucket i is an ordered
+ * run of bucket_len[i] atomic parameters. sizes[] holds the element count of
+ * every parameter, bucket after bucket; loads[] (NULL: the sizes) holds its
+ * load W(p). On return, cuts[i*(ranks+1) + r] .. cuts[i*(ranks+1) + r+1] - 1
+ * are the parameters of bucket i that rank r owns (cuts are parameter indices
+ * within the bucket: 0 first, bucket_len[i] last, non-decreasing), and
+ * rank_loads[r] (if not NULL) is rank r's total load. Errors: INVALID_ARG
+ * (null sizes, bucket_len or cuts; n_buckets < 1; ranks outside [1, 2^20];
+ * an empty bucket; a size outside [1, 2^40]; a negative or non-finite load;
+ * alpha outside [0, 1]). */
+
+/* The Start_Index rule without load balancing (Canzona analysis page,
+ * section 3.4, "Paradigm 3: Static Partitioning"): with S = |B_i| / R, a
+ * parameter whose first element lies in [r S, (r+1) S) of its bucket belongs
+ * to rank r (evaluated exactly, in integers). */
+muon_status muon_dp_partition_static(const int64_t* sizes, const double* loads, const int32_t* bucket_len,
+                                     int32_t n_buckets, int32_t ranks, int32_t* cuts, double* rank_loads);
+
+/* The alpha-Balanced Greedy LPT algorithm (same section, "Algorithm 1"):
+ * buckets in descending load order (equal loads keep their order); per bucket,
+ * deficits d_r = max(0, mu - L_r) against the mean load mu, the target share
+ * v_r = (1 - alpha)/R + alpha d_r / sum(d) (1/R when every deficit is 0), and
+ * the cut of rank r < R-1 at the parameter boundary whose cumulative load is
+ * closest to the cumulative target (the earlier one on a tie, never before
+ * rank r-1's cut); the last rank takes the rest. O(N log N + N R log P) for N
+ * buckets of at most P parameters. */
+muon_status muon_dp_partition(const int64_t* sizes, const double* loads, const int32_t* bucket_len,
+                              int32_t n_buckets, int32_t ranks, double alpha, int32_t* cuts, double* rank_loads);
+
 #ifdef __cplusplus
 }
 #endif

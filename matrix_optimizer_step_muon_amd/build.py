@@ -54,10 +54,12 @@ def build(verbose: bool = True) -> str:
     cc = hipcc()
     k_obj = os.path.join(BUILD, "muon_kernels.o")
     a_obj = os.path.join(BUILD, "muon_api.o")
+    p_obj = os.path.join(BUILD, "muon_partition.o")
     _run([cc, *COMMON, *DEVICE_FLAGS, "-c", os.path.join(CSRC, "muon_kernels.hip"), "-o", k_obj])
     _run([cc, *COMMON, "-c", os.path.join(CSRC, "muon_api.cpp"), "-o", a_obj])
+    _run([cc, *COMMON, "-c", os.path.join(CSRC, "muon_partition.cpp"), "-o", p_obj])
     tmp = LIB + ".tmp"
-    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, k_obj, a_obj,
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, k_obj, a_obj, p_obj,
           "-Wl,-soname,libmuon.so", "-Wl,-rpath,/opt/rocm/lib"])
     os.replace(tmp, LIB)
     return LIB

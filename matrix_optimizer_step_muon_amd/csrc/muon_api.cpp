@@ -44,6 +44,9 @@ constexpr int32_t kMaxNsSteps = 1000;
 
 }  // namespace
 
+// The error path of the other translation units (muon_partition.cpp).
+muon_status muon_fail_message(muon_status st, const char* msg) { return fail(st, msg); }
+
 struct muon_plan_s {
   muon_hparams hp{};
   int dtype = 1;       // muon_dtype: the storage types of w, g, m, delta

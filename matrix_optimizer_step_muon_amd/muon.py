@@ -51,7 +51,8 @@ _lib = None
 EXPORTS = ("muon_hparams_default", "muon_plan", "muon_plan_workspace_bytes", "muon_step",
            "muon_plan_destroy", "muon_last_error", "muon_plan_set_timing",
            "muon_plan_kernel_times", "muon_plan_reset_timing", "muon_plan_info",
-           "muon_apply_plan", "muon_apply", "muon_apply_plan_destroy")
+           "muon_apply_plan", "muon_apply", "muon_apply_plan_destroy",
+           "muon_dp_partition_static", "muon_dp_partition")
 
 
 def lib() -> ctypes.CDLL:
@@ -79,6 +80,9 @@ def lib() -> ctypes.CDLL:
     L.muon_apply_plan.argtypes = [ctypes.POINTER(muon_shard), c_i32, c_i32, ctypes.POINTER(c_vp)]
     L.muon_apply.argtypes = [c_vp, c_vp]
     L.muon_apply_plan_destroy.argtypes = [c_vp]
+    part = [ctypes.POINTER(c_i64), ctypes.POINTER(ctypes.c_double), ctypes.POINTER(c_i32), c_i32, c_i32]
+    L.muon_dp_partition_static.argtypes = part + [ctypes.POINTER(c_i32), ctypes.POINTER(ctypes.c_double)]
+    L.muon_dp_partition.argtypes = part + [ctypes.c_double, ctypes.POINTER(c_i32), ctypes.POINTER(ctypes.c_double)]
     for name in EXPORTS:
         if name != "muon_last_error":
             getattr(L, name).restype = c_int
@@ -286,3 +290,34 @@ class ApplyPlan:
 
     def __exit__(self, *exc):
         self.close()
+
+
+def dp_partition(buckets: Sequence[Sequence[int]], ranks: int, alpha: Optional[float] = 1.0,
+                 loads: Optional[Sequence[Sequence[float]]] = None):
+    """Data-parallel static partition of a parameter buffer (host only).
+
+    ``buckets``: per bucket, the element counts of its parameters in buffer
+    order. ``loads``: the same shape, each parameter's load (default: its
+    element count). ``alpha``: the alpha-Balanced Greedy LPT algorithm with that
+    alpha, or None for the Start_Index rule without load balancing. Returns
+    ``(cuts, rank_loads)``: per bucket the ranks + 1 parameter-index cuts (rank
+    r owns parameters cuts[r] .. cuts[r+1] - 1), and each rank's total load."""
+    lens = [len(b) for b in buckets]
+    flat = [int(x) for b in buckets for x in b]
+    n, nb = len(flat), len(lens)
+    sz = (ctypes.c_int64 * max(n, 1))(*flat)
+    ld = None
+    if loads is not None:
+        fl = [float(x) for b in loads for x in b]
+        if len(fl) != n:
+            raise MuonError(-1, "loads must have the shape of buckets")
+        ld = (ctypes.c_double * max(n, 1))(*fl)
+    bl = (ctypes.c_int32 * max(nb, 1))(*lens)
+    cuts = (ctypes.c_int32 * max(nb * (ranks + 1), 1))()
+    rl = (ctypes.c_double * max(ranks, 1))()
+    if alpha is None:
+        check(lib().muon_dp_partition_static(sz, ld, bl, nb, ranks, cuts, rl))
+    else:
+        check(lib().muon_dp_partition(sz, ld, bl, nb, ranks, float(alpha), cuts, rl))
+    out = [list(cuts[i * (ranks + 1):(i + 1) * (ranks + 1)]) for i in range(nb)]
+    return out, list(rl[:ranks])

@@ -167,3 +167,41 @@ def rel_fro(x: np.ndarray, ref: np.ndarray) -> float:
     if den == 0.0:
         return float(num)
     return float(num / den)
+
+
+# ------------------------------------------------------- parameter buffers
+
+QWEN3_32B_HIDDEN = 5120
+QWEN3_VOCAB = 151936
+
+
+def qwen3_32b_param_buffer(tp: int = 1, bucket_elems: int = 40_000_000) -> List[List[Tuple[int, ...]]]:
+    """Shapes of a Qwen3-32B-shaped parameter buffer, split into buckets.
+
+    Per decoder layer: q 8192 x 5120, k and v 1024 x 5120, o 5120 x 8192, gate
+    and up 25600 x 5120, down 5120 x 25600 (the shapes of the Qwen3-32B layer
+    workload), the q and k norms (128) and the two layer norms (5120); 64
+    layers, the input embedding and the output projection (vocabulary x 5120)
+    and the final norm. With tp > 1 this is one tensor-parallel rank's local
+    buffer: column-parallel weights (q, k, v, gate, up, the embeddings) keep
+    1/tp of their rows, row-parallel ones (o, down) 1/tp of their columns, and
+    norms are whole. Parameters enter the buffer in reverse order (the order in
+    which gradients become ready) and a bucket closes once it holds at least
+    bucket_elems elements; a parameter is never split."""
+    H, V = QWEN3_32B_HIDDEN, QWEN3_VOCAB
+    col = lambda r, c: (r // tp, c)
+    row = lambda r, c: (r, c // tp)
+    layer = [col(8192, H), col(1024, H), col(1024, H), row(H, 8192), col(25600, H), col(25600, H),
+             row(H, 25600), (128,), (128,), (H,), (H,)]
+    params = [col(V, H)] + layer * 64 + [(H,), col(V, H)]
+    buckets: List[List[Tuple[int, ...]]] = [[]]
+    filled = 0
+    for shape in reversed(params):
+        buckets[-1].append(shape)
+        filled += int(np.prod(shape))
+        if filled >= bucket_elems:
+            buckets.append([])
+            filled = 0
+    if not buckets[-1]:
+        buckets.pop()
+    return buckets
