@@ -324,6 +324,47 @@ def dp_partition_measure(mu, wl, ranks=32, tp=8):
     return out
 
 
+def tp_micro_groups_measure(mu, ranks=8):
+    """The TP micro-group schedule (host) of a Qwen3-32B-shaped model's
+    TP-split tensors (64 layers of q, k, v, o, gate, up, down) over `ranks` host
+    ranks, cost = element count, C_max = the largest tensor's cost.
+
+    Groups run one after another and each waits for its slowest host rank, so
+    the schedule's cost is the sum over groups of the largest rank load. The
+    report gives that sum over the sum of the mean rank loads (1.0 = every
+    group perfectly balanced), for the hosted elements and the hosted Muon
+    FLOPs, against one group per layer with hosts dealt round-robin, plus the
+    group count and the planner's time."""
+    import math
+    shapes = [(8192, 5120), (1024, 5120), (1024, 5120), (5120, 8192), (25600, 5120), (25600, 5120),
+              (5120, 25600)] * 64
+    numel = [float(math.prod(s)) for s in shapes]
+    flops = [float(nsflops([s], 5)["total"]) for s in shapes]
+
+    def makespan_ratio(groups, loads):
+        worst = mean = 0.0
+        for ids, hosts in groups:
+            tot = [0.0] * ranks
+            for i, h in zip(ids, hosts):
+                tot[h] += loads[i]
+            worst += max(tot)
+            mean += sum(tot) / ranks
+        return round(worst / mean, 3)
+
+    mu.tp_micro_groups(numel, ranks, max(numel))   # first call: loads the library
+    t0 = time.perf_counter()
+    groups = mu.tp_micro_groups(numel, ranks, max(numel))
+    ms = (time.perf_counter() - t0) * 1e3
+    per_layer = [(list(range(7 * l, 7 * l + 7)), [i % ranks for i in range(7 * l, 7 * l + 7)]) for l in range(64)]
+    return {"tensors": len(shapes), "host_ranks": ranks, "c_max": "the largest tensor's element count",
+            "groups": len(groups), "ms": round(ms, 3),
+            "micro_groups": {"makespan_ratio_memory": makespan_ratio(groups, numel),
+                             "makespan_ratio_flops": makespan_ratio(groups, flops)},
+            "per_layer_round_robin": {"groups": len(per_layer),
+                                      "makespan_ratio_memory": makespan_ratio(per_layer, numel),
+                                      "makespan_ratio_flops": makespan_ratio(per_layer, flops)}}
+
+
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "update_kernel_traffic_qwen3_32b_layer.txt")
 KERNEL_SOURCE = os.path.join(ROOT, "matrix_optimizer_step_muon_amd", "csrc", "muon_kernels.hip")
 
@@ -480,6 +521,7 @@ def main():
         print(f"[bench] fp32 master weights: {master['ms_per_step']:.3f} ms per step", file=sys.stderr, flush=True)
 
     dp_part = dp_partition_measure(mu, wl)
+    tp_groups = tp_micro_groups_measure(mu)
 
     tp_apply = None
     if not args.no_tp_apply:
@@ -553,6 +595,7 @@ def main():
         "kernels": per_kernel,
         "master_weights": master,
         "dp_partition": dp_part,
+        "tp_micro_groups": tp_groups,
         "tp_apply": tp_apply,
         "momentum_hbm": {"achieved_gbs": round(mom_gbs, 1) if mom_gbs else None,
                          "peak_gbs": HBM_PEAK_GBS, "alg_bytes_per_elem": 4 * elem},

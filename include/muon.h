@@ -249,6 +249,22 @@ muon_status muon_dp_partition_static(const int64_t* sizes, const double* loads, 
 muon_status muon_dp_partition(const int64_t* sizes, const double* loads, const int32_t* bucket_len,
                               int32_t n_buckets, int32_t ranks, double alpha, int32_t* cuts, double* rank_loads);
 
+/* TP micro groups (host only; Canzona analysis page, section 3.4, "The TP
+ * Hierarchical Partitioning and Scheduling", the LPT with greedy rollback and
+ * its min-heap solver). n tensors with costs cost[i] (their ID is i) are
+ * sorted by (cost, ID) descending and packed, in that order, into groups: a
+ * tensor joins the current group if the min-heap LPT assignment of the group
+ * (by cost descending, each tensor to the least-loaded of `ranks` host ranks,
+ * the lower rank on a tie) keeps every rank's load within c_max; otherwise the
+ * group closes and the tensor starts the next one (a tensor heavier than
+ * c_max alone forms its own group). On return order[] holds the IDs in
+ * schedule order (every group a consecutive run), group_of[i] and host_of[i]
+ * the group and host rank of tensor i, and *n_groups the number of groups.
+ * Errors: INVALID_ARG (null pointers, n < 1, ranks outside [1, 2^20], c_max
+ * not finite and > 0, a negative or non-finite cost). */
+muon_status muon_tp_micro_groups(const double* cost, int32_t n, int32_t ranks, double c_max, int32_t* order,
+                                 int32_t* group_of, int32_t* host_of, int32_t* n_groups);
+
 #ifdef __cplusplus
 }
 #endif

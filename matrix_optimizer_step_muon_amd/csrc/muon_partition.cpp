@@ -1,6 +1,8 @@
-// DP static partition (host only): which whole parameters each data-parallel
-// rank owns. This is the planner in front of the step: a rank's share of the
-// parameters becomes the batch it hands to muon_plan.
+// Static plans of the distributed step (host only).
+//
+// DP static partition: which whole parameters each data-parallel rank owns.
+// This is the planner in front of the step: a rank's share of the parameters
+// becomes the batch it hands to muon_plan.
 //
 // Canzona analysis page (paper-graph-ui), section 3.4:
 // - "Paradigm 3: Static Partitioning": a parameter belongs to the rank whose
@@ -12,6 +14,11 @@
 //   shares, and cuts at the parameter boundaries closest to the cumulative
 //   targets (muon_dp_partition).
 //
+// TP micro groups (same section, "The TP Hierarchical Partitioning and
+// Scheduling"): tensors sorted by (cost, ID) descending, packed greedily into
+// groups with a rollback when the min-heap LPT assignment of the tentative
+// group to the host ranks exceeds C_max (muon_tp_micro_groups).
+//
 // Cuts are parameter indices within a bucket, non-decreasing, with the tie in
 // "closest" going to the earlier boundary. The sums are formed in the order
 // the algorithm states them, and without contraction into fused multiply-adds,
@@ -20,8 +27,11 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <functional>
 #include <numeric>
+#include <queue>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "muon.h"
@@ -158,6 +168,69 @@ muon_status muon_dp_partition(const int64_t* sizes, const double* loads, const i
     L[ranks - 1] += phi[m] - phi[c[ranks - 1]];
   }
   if (rank_loads) sum_rank_loads(w, cuts, ranks, rank_loads);
+  return MUON_OK;
+}
+
+namespace {
+
+// LPT of the items (tensor IDs, in the order they joined the group) on R host
+// ranks: by cost, descending (stable), each to the least-loaded rank (lowest
+// index on a tie). Writes the host of each item into host_of (by ID) when it
+// is not null, and returns the largest load.
+double min_heap_solve(const std::vector<int32_t>& items, const double* cost, int32_t ranks, int32_t* host_of,
+                      std::vector<int32_t>& tmp) {
+  tmp = items;
+  std::stable_sort(tmp.begin(), tmp.end(), [&](int32_t a, int32_t b) { return cost[a] > cost[b]; });
+  using Slot = std::pair<double, int32_t>;
+  std::priority_queue<Slot, std::vector<Slot>, std::greater<Slot>> pq;
+  for (int32_t r = 0; r < ranks; ++r) pq.push({0.0, r});
+  double worst = 0.0;
+  for (int32_t id : tmp) {
+    Slot s = pq.top();
+    pq.pop();
+    if (host_of) host_of[id] = s.second;
+    s.first = s.first + cost[id];
+    worst = std::max(worst, s.first);
+    pq.push(s);
+  }
+  return worst;
+}
+
+}  // namespace
+
+muon_status muon_tp_micro_groups(const double* cost, int32_t n, int32_t ranks, double c_max, int32_t* order,
+                                 int32_t* group_of, int32_t* host_of, int32_t* n_groups) {
+  if (!cost || !order || !group_of || !host_of || !n_groups)
+    return muon_fail_message(MUON_ERR_INVALID_ARG, "a pointer argument is NULL");
+  if (n < 1) return muon_fail_message(MUON_ERR_INVALID_ARG, "n must be >= 1");
+  if (ranks < 1 || ranks > (1 << 20)) return muon_fail_message(MUON_ERR_INVALID_ARG, "ranks must be in [1, 2^20]");
+  if (!(std::isfinite(c_max) && c_max > 0.0)) return muon_fail_message(MUON_ERR_INVALID_ARG, "c_max must be finite and > 0");
+  for (int32_t i = 0; i < n; ++i)
+    if (!(std::isfinite(cost[i]) && cost[i] >= 0.0))
+      return muon_fail_message(MUON_ERR_INVALID_ARG, "costs must be finite and >= 0");
+  // Phase 1: (cost, ID) descending.
+  std::iota(order, order + n, 0);
+  std::sort(order, order + n, [&](int32_t a, int32_t b) { return cost[a] > cost[b] || (cost[a] == cost[b] && a > b); });
+  // Phase 2: greedy packing with rollback.
+  std::vector<int32_t> curr, tmp;
+  int32_t g = 0;
+  auto close = [&]() {
+    min_heap_solve(curr, cost, ranks, host_of, tmp);
+    for (int32_t id : curr) group_of[id] = g;
+    ++g;
+  };
+  for (int32_t j = 0; j < n; ++j) {
+    const int32_t p = order[j];
+    curr.push_back(p);
+    if (curr.size() == 1) continue;  // a group's first tensor is always taken
+    if (min_heap_solve(curr, cost, ranks, nullptr, tmp) > c_max) {
+      curr.pop_back();
+      close();
+      curr.assign(1, p);
+    }
+  }
+  close();
+  *n_groups = g;
   return MUON_OK;
 }
 

@@ -52,7 +52,7 @@ EXPORTS = ("muon_hparams_default", "muon_plan", "muon_plan_workspace_bytes", "mu
            "muon_plan_destroy", "muon_last_error", "muon_plan_set_timing",
            "muon_plan_kernel_times", "muon_plan_reset_timing", "muon_plan_info",
            "muon_apply_plan", "muon_apply", "muon_apply_plan_destroy",
-           "muon_dp_partition_static", "muon_dp_partition")
+           "muon_dp_partition_static", "muon_dp_partition", "muon_tp_micro_groups")
 
 
 def lib() -> ctypes.CDLL:
@@ -83,6 +83,9 @@ def lib() -> ctypes.CDLL:
     part = [ctypes.POINTER(c_i64), ctypes.POINTER(ctypes.c_double), ctypes.POINTER(c_i32), c_i32, c_i32]
     L.muon_dp_partition_static.argtypes = part + [ctypes.POINTER(c_i32), ctypes.POINTER(ctypes.c_double)]
     L.muon_dp_partition.argtypes = part + [ctypes.c_double, ctypes.POINTER(c_i32), ctypes.POINTER(ctypes.c_double)]
+    L.muon_tp_micro_groups.argtypes = [ctypes.POINTER(ctypes.c_double), c_i32, c_i32, ctypes.c_double,
+                                       ctypes.POINTER(c_i32), ctypes.POINTER(c_i32), ctypes.POINTER(c_i32),
+                                       ctypes.POINTER(c_i32)]
     for name in EXPORTS:
         if name != "muon_last_error":
             getattr(L, name).restype = c_int
@@ -321,3 +324,20 @@ def dp_partition(buckets: Sequence[Sequence[int]], ranks: int, alpha: Optional[f
         check(lib().muon_dp_partition(sz, ld, bl, nb, ranks, float(alpha), cuts, rl))
     out = [list(cuts[i * (ranks + 1):(i + 1) * (ranks + 1)]) for i in range(nb)]
     return out, list(rl[:ranks])
+
+
+def tp_micro_groups(costs: Sequence[float], ranks: int, c_max: float):
+    """TP micro-group schedule (host only). Returns the groups in order, each
+    as ``(tensor IDs, host ranks)``, the IDs in schedule order."""
+    n = len(costs)
+    c = (ctypes.c_double * max(n, 1))(*[float(x) for x in costs])
+    order = (ctypes.c_int32 * max(n, 1))()
+    group_of = (ctypes.c_int32 * max(n, 1))()
+    host_of = (ctypes.c_int32 * max(n, 1))()
+    ng = ctypes.c_int32()
+    check(lib().muon_tp_micro_groups(c, n, ranks, float(c_max), order, group_of, host_of, ctypes.byref(ng)))
+    groups = [([], []) for _ in range(ng.value)]
+    for i in order[:n]:
+        groups[group_of[i]][0].append(i)
+        groups[group_of[i]][1].append(host_of[i])
+    return groups
