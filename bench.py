@@ -65,6 +65,8 @@ def parse():
     ap.add_argument("--run-steps", type=int, default=10)
     ap.add_argument("--no-master-weights", action="store_true",
                     help="skip the step with fp32 master weights and momentum (MUON_BF16_F32_MASTER)")
+    ap.add_argument("--no-mfma-probe", action="store_true",
+                    help="skip the MFMA throughput probe")
     ap.add_argument("--no-tp-apply", action="store_true",
                     help="skip the measurement of the tensor-parallel local update (muon_apply)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -365,6 +367,33 @@ def tp_micro_groups_measure(mu, ranks=8):
                                       "makespan_ratio_flops": makespan_ratio(per_layer, flops)}}
 
 
+def mfma_probe_measure(mu, stream, reps=6, iters=400_000):
+    """The bf16 MFMA rate the chip sustains on random register data: two
+    workgroups of 4 waves per CU issuing 32x32x16 MFMAs back to back
+    (muon_mfma_probe), `reps` timed launches after one untimed, with the GPU
+    clock sampled meanwhile."""
+    import torch
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks = 2 * n_cu
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    mu.mfma_probe(out, blocks, iters // 10, stream)
+    torch.cuda.synchronize()
+    sampler = GpuSampler(torch.cuda.get_device_properties(0))
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with sampler:
+        a.record(stream)
+        for _ in range(reps):
+            mu.mfma_probe(out, blocks, iters, stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    flops = blocks * 4 * iters * 8 * 32768
+    clock = sampler.summary()
+    return {"tflops": round(flops / (ms / 1e3) / 1e12, 1), "avg_launch_ms": round(ms, 3),
+            "gfx_mhz_median": clock.get("gfx_mhz_median"), "socket_power_w_median": clock.get("socket_power_w_median"),
+            "what": "bf16 32x32x16 MFMAs back to back on random register operands, 8 waves per CU"}
+
+
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "update_kernel_traffic_qwen3_32b_layer.txt")
 KERNEL_SOURCE = os.path.join(ROOT, "matrix_optimizer_step_muon_amd", "csrc", "muon_kernels.hip")
 
@@ -520,6 +549,9 @@ def main():
                                         nsflops(wload.shapes, wload.ns_steps)["total"])
         print(f"[bench] fp32 master weights: {master['ms_per_step']:.3f} ms per step", file=sys.stderr, flush=True)
 
+    probe = None if args.no_mfma_probe else mfma_probe_measure(mu, stream)
+    if probe:
+        print(f"[bench] mfma probe: {probe['tflops']:.0f} TFLOP/s", file=sys.stderr, flush=True)
     dp_part = dp_partition_measure(mu, wl)
     tp_groups = tp_micro_groups_measure(mu)
 
@@ -594,6 +626,10 @@ def main():
         },
         "kernels": per_kernel,
         "master_weights": master,
+        "mfma_probe": probe,
+        # The step's rate against the bf16 MFMA rate the chip sustains on
+        # random data under its power limit (the probe above).
+        "fraction_of_mfma_probe": round(tflops / probe["tflops"], 4) if probe else None,
         "dp_partition": dp_part,
         "tp_micro_groups": tp_groups,
         "tp_apply": tp_apply,

@@ -217,6 +217,18 @@ muon_status muon_apply(muon_apply_plan_t plan, void* stream);
 muon_status muon_apply_plan_destroy(muon_apply_plan_t plan);
 
 /* ---------------------------------------------------------------------------
+ * MFMA throughput probe (measurement, not part of the step). Enqueues one
+ * kernel of `blocks` workgroups of 4 waves on `stream`; every wave issues
+ * iters * 8 bf16 MFMAs of 32 x 32 x 16 (32768 flops each) back to back on
+ * random register data and stores one sum per lane into out (a device buffer
+ * of blocks * 256 floats). Timed by the caller, it gives the bf16 MFMA rate
+ * the chip sustains on random data under its power limit, against which the
+ * step's rate can be read. It is a measurement aid, not an operation of the
+ * pages' method. Errors:
+ * INVALID_ARG (out NULL, blocks outside [1, 2^20], iters < 1), HIP. */
+muon_status muon_mfma_probe(float* out, int32_t blocks, int32_t iters, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Data-parallel static partition: which whole parameters each DP rank owns
  * (host only, no GPU). A rank's share is the batch it passes to muon_plan.
  *

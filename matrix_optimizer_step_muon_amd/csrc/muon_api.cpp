@@ -766,6 +766,14 @@ muon_status muon_apply(muon_apply_plan_t p, void* stream) {
   return e == hipSuccess ? MUON_OK : hip_fail(e, "kernel launch");
 }
 
+muon_status muon_mfma_probe(float* out, int32_t blocks, int32_t iters, void* stream) {
+  if (!out) return fail(MUON_ERR_INVALID_ARG, "out is NULL");
+  if (blocks < 1 || blocks > (1 << 20)) return fail(MUON_ERR_INVALID_ARG, "blocks must be in [1, 2^20]");
+  if (iters < 1) return fail(MUON_ERR_INVALID_ARG, "iters must be >= 1");
+  const hipError_t e = muon::launch_mfma_probe(out, blocks, iters, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MUON_OK : hip_fail(e, "kernel launch");
+}
+
 muon_status muon_apply_plan_destroy(muon_apply_plan_t p) {
   if (!p) return MUON_OK;
   hipError_t e = hipDeviceSynchronize();

@@ -104,6 +104,8 @@ hipError_t launch_momentum(int dtype, const EwArgs& args, int32_t n_blocks, hipS
 hipError_t launch_norm(const MatDev* mats, const float* partials, float* scale, int32_t n_mats,
                        float eps, hipStream_t s);
 hipError_t launch_apply(int dtype, const EwArgs& args, int32_t n_blocks, hipStream_t s);
+// blocks workgroups of 256 threads; out holds blocks * 256 floats.
+hipError_t launch_mfma_probe(float* out, int32_t blocks, int32_t iters, hipStream_t s);
 // prefix[i] = first tile of shard i (prefix[n] = n_blocks).
 hipError_t launch_shard_apply(int dtype, const ShardDev* shards, const int32_t* prefix, int32_t n,
                               int32_t n_blocks, hipStream_t s);

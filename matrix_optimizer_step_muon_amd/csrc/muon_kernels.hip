@@ -2016,6 +2016,48 @@ __global__ void __launch_bounds__(256) shard_apply_kernel(const ShardDev* shards
   }
 }
 
+// MFMA throughput probe (measurement only): v_mfma_f32_32x32x16_bf16 back to
+// back on register operands holding random bf16 values (xorshift of the lane
+// and workgroup), 8 independent accumulators per wave so that no MFMA waits
+// for another's result, and a different operand pair for consecutive MFMAs so
+// that the inputs toggle as they do in a GEMM. It measures what the chip
+// sustains on random data under its power limit: the ceiling the GEMM kernels
+// run against. The sums are stored so that nothing is optimised away.
+__global__ void __launch_bounds__(256) mfma_probe_kernel(float* out, int iters) {
+  const int tid = threadIdx.x;
+  uint32_t h = (blockIdx.x * 256u + (uint32_t)tid) * 2654435761u + 12345u;
+  auto rnd = [&]() {
+    h ^= h << 13;
+    h ^= h >> 17;
+    h ^= h << 5;
+    return h;
+  };
+  bf16x8 a[4], b[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      a[k][e] = (__bf16)((float)((int)(rnd() & 0xffffu) - 32768) * (1.f / 32768.f));
+      b[k][e] = (__bf16)((float)((int)(rnd() & 0xffffu) - 32768) * (1.f / 32768.f));
+    }
+  f32x16 acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[j][e] = 0.f;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j & 3], b[(j + (j >> 2)) & 3], acc[j], 0, 0, 0);
+  }
+  float sum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sum += acc[j][e];
+  out[(size_t)blockIdx.x * 256 + tid] = sum;
+}
+
 // ------------------------------------------------------------ launchers
 
 hipError_t launch_momentum(int dtype, const EwArgs& args, int32_t n_blocks, hipStream_t s) {
@@ -2028,6 +2070,11 @@ hipError_t launch_momentum(int dtype, const EwArgs& args, int32_t n_blocks, hipS
 hipError_t launch_norm(const MatDev* mats, const float* partials, float* scale, int32_t n_mats,
                        float eps, hipStream_t s) {
   hipLaunchKernelGGL(norm_kernel, dim3(n_mats), dim3(256), 0, s, mats, partials, scale, eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_mfma_probe(float* out, int32_t blocks, int32_t iters, hipStream_t s) {
+  hipLaunchKernelGGL(mfma_probe_kernel, dim3(blocks), dim3(256), 0, s, out, iters);
   return hipGetLastError();
 }
 

@@ -52,7 +52,7 @@ EXPORTS = ("muon_hparams_default", "muon_plan", "muon_plan_workspace_bytes", "mu
            "muon_plan_destroy", "muon_last_error", "muon_plan_set_timing",
            "muon_plan_kernel_times", "muon_plan_reset_timing", "muon_plan_info",
            "muon_apply_plan", "muon_apply", "muon_apply_plan_destroy",
-           "muon_dp_partition_static", "muon_dp_partition", "muon_tp_micro_groups")
+           "muon_dp_partition_static", "muon_dp_partition", "muon_tp_micro_groups", "muon_mfma_probe")
 
 
 def lib() -> ctypes.CDLL:
@@ -83,6 +83,7 @@ def lib() -> ctypes.CDLL:
     part = [ctypes.POINTER(c_i64), ctypes.POINTER(ctypes.c_double), ctypes.POINTER(c_i32), c_i32, c_i32]
     L.muon_dp_partition_static.argtypes = part + [ctypes.POINTER(c_i32), ctypes.POINTER(ctypes.c_double)]
     L.muon_dp_partition.argtypes = part + [ctypes.c_double, ctypes.POINTER(c_i32), ctypes.POINTER(ctypes.c_double)]
+    L.muon_mfma_probe.argtypes = [c_vp, c_i32, c_i32, c_vp]
     L.muon_tp_micro_groups.argtypes = [ctypes.POINTER(ctypes.c_double), c_i32, c_i32, ctypes.c_double,
                                        ctypes.POINTER(c_i32), ctypes.POINTER(c_i32), ctypes.POINTER(c_i32),
                                        ctypes.POINTER(c_i32)]
@@ -341,3 +342,16 @@ def tp_micro_groups(costs: Sequence[float], ranks: int, c_max: float):
         groups[group_of[i]][0].append(i)
         groups[group_of[i]][1].append(host_of[i])
     return groups
+
+
+def mfma_probe(out, blocks: int, iters: int, stream=None) -> None:
+    """Enqueues the MFMA throughput probe: ``blocks`` workgroups, each wave
+    issuing ``iters`` * 8 bf16 32x32x16 MFMAs; ``out`` is a float32 device
+    tensor of at least blocks * 256 elements."""
+    import torch
+    if out.dtype != torch.float32 or not out.is_cuda or out.numel() < blocks * 256:
+        raise MuonError(-1, "out must be a float32 device tensor of blocks * 256 elements")
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    check(lib().muon_mfma_probe(ctypes.c_void_p(out.data_ptr()), int(blocks), int(iters),
+                                ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))))
