@@ -543,23 +543,27 @@ def main():
         print(f"[bench] protocol: {args.runs} runs x {args.run_steps} steps, mean {proto['mean_ms']:.3f} ms",
               file=sys.stderr, flush=True)
 
+    def aux(name, fn):
+        """An auxiliary measurement: a failure is recorded in the line instead
+        of ending the run, so the headline measurement above is never lost."""
+        try:
+            res = fn()
+            print(f"[bench] {name}: {json.dumps(res)[:200]}", file=sys.stderr, flush=True)
+            return res
+        except Exception as e:  # noqa: BLE001 - any failure is reported, not raised
+            print(f"[bench] {name} failed: {e}", file=sys.stderr, flush=True)
+            return {"error": f"{type(e).__name__}: {e}"[:300]}
+
     master = None
     if wload.dtype == "bf16" and not args.no_master_weights:
-        master = master_weights_measure(mu, wload, stream, args.steps, args.warmup,
-                                        nsflops(wload.shapes, wload.ns_steps)["total"])
-        print(f"[bench] fp32 master weights: {master['ms_per_step']:.3f} ms per step", file=sys.stderr, flush=True)
-
-    probe = None if args.no_mfma_probe else mfma_probe_measure(mu, stream)
-    if probe:
-        print(f"[bench] mfma probe: {probe['tflops']:.0f} TFLOP/s", file=sys.stderr, flush=True)
-    dp_part = dp_partition_measure(mu, wl)
-    tp_groups = tp_micro_groups_measure(mu)
-
+        master = aux("fp32 master weights", lambda: master_weights_measure(
+            mu, wload, stream, args.steps, args.warmup, nsflops(wload.shapes, wload.ns_steps)["total"]))
+    probe = None if args.no_mfma_probe else aux("mfma probe", lambda: mfma_probe_measure(mu, stream))
+    dp_part = aux("dp partition", lambda: dp_partition_measure(mu, wl))
+    tp_groups = aux("tp micro groups", lambda: tp_micro_groups_measure(mu))
     tp_apply = None
     if not args.no_tp_apply:
-        tp_apply = tp_apply_measure(mu, wload.shapes, wload.dtype, stream)
-        print(f"[bench] tp apply: {tp_apply['avg_launch_ms']:.3f} ms, {tp_apply['achieved_gbs']:.0f} GB/s",
-              file=sys.stderr, flush=True)
+        tp_apply = aux("tp apply", lambda: tp_apply_measure(mu, wload.shapes, wload.dtype, stream))
 
     fl = nsflops(wload.shapes, wload.ns_steps)
     tflops = fl["total"] / (ms_per_step / 1e3) / 1e12
@@ -629,7 +633,7 @@ def main():
         "mfma_probe": probe,
         # The step's rate against the bf16 MFMA rate the chip sustains on
         # random data under its power limit (the probe above).
-        "fraction_of_mfma_probe": round(tflops / probe["tflops"], 4) if probe else None,
+        "fraction_of_mfma_probe": round(tflops / probe["tflops"], 4) if probe and probe.get("tflops") else None,
         "dp_partition": dp_part,
         "tp_micro_groups": tp_groups,
         "tp_apply": tp_apply,
@@ -645,7 +649,11 @@ def main():
     if not args.no_cpu_baseline:
         idx = [int(x) for x in args.cpu_sample.split(",") if x != ""]
         print(f"[bench] cpu baseline: oracle on matrices {idx}", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(wload, idx)
+        try:
+            out["cpu_baseline"] = cpu_baseline(wload, idx)
+        except Exception as e:  # noqa: BLE001 - the line is still printed
+            print(f"[bench] cpu baseline failed: {e}", file=sys.stderr, flush=True)
+            out["cpu_baseline"] = {"value": None, "error": f"{type(e).__name__}: {e}"[:300]}
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
