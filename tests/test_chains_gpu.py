@@ -39,18 +39,18 @@ def _with_chains(n, fn):
     return _with_env("MUON_CHAINS", n, fn)
 
 
-@pytest.mark.parametrize("split_prologue", [1, 0])
-def test_one_and_two_chains_agree_bitwise(split_prologue):
+@pytest.mark.parametrize("chains,split_prologue", [(2, 1), (2, 0), (3, 1)])
+def test_one_and_several_chains_agree_bitwise(chains, split_prologue):
     w = wl.custom_workload("chains", SHAPES, "bf16", seed=51)
     inputs = wl.generate(w)
     hp = w.hparams()
-    log(f"case chains 1 vs 2, split prologue {split_prologue}")
+    log(f"case chains 1 vs {chains}, split prologue {split_prologue}")
     one = _with_chains(1, lambda: gpu_step(inputs, "bf16", hp, steps=2))
-    two = _with_env("MUON_SPLIT_PROLOGUE", split_prologue,
-                    lambda: _with_chains(2, lambda: gpu_step(inputs, "bf16", hp, steps=2)))
-    for i, (a, b) in enumerate(zip(one, two)):
+    many = _with_env("MUON_SPLIT_PROLOGUE", split_prologue,
+                     lambda: _with_chains(chains, lambda: gpu_step(inputs, "bf16", hp, steps=2)))
+    for i, (a, b) in enumerate(zip(one, many)):
         for name, x, y in zip(("W'", "M'", "delta"), a, b):
-            assert np.array_equal(x, y), f"matrix {i} {SHAPES[i]}: {name} differs between one and two chains"
+            assert np.array_equal(x, y), f"matrix {i} {SHAPES[i]}: {name} differs between 1 and {chains} chains"
 
 
 def test_step_on_a_side_stream_is_joined():
