@@ -110,7 +110,14 @@ def cpu_baseline(wload, indices):
     dt = time.perf_counter() - t0
     flops = sum(ref.step_flops(*wload.shapes[i], wload.ns_steps) for i in indices)
     shapes = [f"{wload.shapes[i][0]}x{wload.shapes[i][1]}" for i in indices]
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), None)
+    except OSError:
+        pass
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads or os.cpu_count(),
+            "host_cpus": os.cpu_count(), "cpu_model": model,
             "kind": "oracle", "seconds": round(dt, 3),
             "sample": f"fp64 numpy oracle, full step on {len(indices)} of {len(wload.shapes)} "
                       f"matrices ({', '.join(shapes)}) of the same workload"}

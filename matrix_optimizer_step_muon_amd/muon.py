@@ -153,6 +153,17 @@ def _batch_dtype(W, G, M, D) -> int:
     raise MuonError(-1, "W, M and delta must share G's dtype, or be fp32 with a bf16 G")
 
 
+def plan(mats: Iterable[Sequence], *, dtype: Optional[int] = None, **hparams) -> "Plan":
+    """``Plan(mats, **hparams)``, checking that the tensors' dtypes give
+    ``dtype`` (MUON_F32, MUON_BF16 or MUON_BF16_F32_MASTER) when it is given."""
+    p = Plan(mats, **hparams)
+    if dtype is not None and p.hparams.dtype != dtype:
+        got = p.hparams.dtype
+        p.close()
+        raise MuonError(-1, f"the tensors give dtype {got}, not {dtype}")
+    return p
+
+
 class Plan:
     """A static plan over a batch of ``(W, G, M[, delta])`` device tensors.
 
