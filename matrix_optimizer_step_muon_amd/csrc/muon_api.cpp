@@ -324,11 +324,10 @@ muon_status muon_plan(const muon_matrix* mats, int32_t n, const muon_hparams* hp
   // XCDs, share the column operand's panels in the Infinity Cache. Tuning
   // knobs: MUON_BLOCK=RxC sets the block shape in tiles, and
   // MUON_BLOCK_ORDER=0 walks blocks row-major instead.
-  // With several chains their kernels run side by side and each gets about
-  // half of every XCD's CUs: 4 x 4 blocks, 1.2% less step time than 4 x 8 on
-  // the Qwen3-32B layer (same box; 2 x 8, 4 x 2, 2 x 4, 3 x 4, 4 x 3, 4 x 6,
-  // 6 x 4 and 8 x 4 are all slower than 4 x 4).
-  int brows = muon::kBlockRows, bcols = C > 1 ? muon::kBlockColsChains : muon::kBlockCols, border = 1;
+  // 4 x 4 blocks: 1.2% less step time than 4 x 8 on the Qwen3-32B layer with
+  // two chains, 0.9% with one (same box; 2 x 8, 4 x 2, 2 x 4, 3 x 4, 4 x 3,
+  // 4 x 6, 6 x 4 and 8 x 4 are all slower than 4 x 4).
+  int brows = muon::kBlockRows, bcols = muon::kBlockCols, border = 1;
   if (const char* v = std::getenv("MUON_BLOCK")) {
     int r = 0, c = 0;
     if (std::sscanf(v, "%dx%d", &r, &c) == 2 && r > 0 && c > 0 && r * c <= 1024) { brows = r; bcols = c; }

@@ -18,13 +18,12 @@ constexpr int kEwTile = 64;     // elementwise kernels: 64 x 64 tiles
 // w % kQueues first (workgroups are dispatched to the 8 XCDs round-robin), then
 // steals from the others. Each queue holds whole blocks of kBlockRows x
 // kBlockCols tiles, so concurrently running tiles on one XCD share operand
-// panels in that XCD's L2. A block matches the CUs one kernel gets on an XCD:
-// 32 tiles when a single chain of launches has the GPU to itself, 16
-// (kBlockRows x kBlockColsChains) when two chains' kernels share it.
+// panels in that XCD's L2. 4 x 4 tiles: half of an XCD's 32 CUs, the share a
+// kernel gets when two chains' kernels run side by side, and also the fastest
+// shape for a single chain.
 constexpr int kQueues = 8;
 constexpr int kBlockRows = 4;
-constexpr int kBlockCols = 8;
-constexpr int kBlockColsChains = 4;
+constexpr int kBlockCols = 4;
 
 // One matrix of the batch as the kernels see it. X is the m x n orientation
 // of U (m = min(rows, cols)): U itself, or U^T when rows > cols.
