@@ -79,3 +79,27 @@ def test_step_on_a_side_stream_is_joined():
     got = _with_chains(2, run)
     for i, (g, ref) in enumerate(zip(got, want)):
         assert np.array_equal(g, ref[0]), f"matrix {i} {SHAPES[i]}: W copied after the step is not the final W"
+
+
+@pytest.mark.parametrize("env", [{"MUON_BLOCK": "2x8"}, {"MUON_BLOCK": "1x1", "MUON_BLOCK_ORDER": "0"},
+                                 {"MUON_BLOCK_PHASES": "4x8,2x4,8x2"}])
+def test_tile_schedule_does_not_change_results(env):
+    """Block shapes and the order blocks are dealt in only move tiles between
+    queues and workgroups; every tile's arithmetic is the same, so the result
+    is bit for bit the default schedule's."""
+    w = wl.custom_workload("schedule", SHAPES, "bf16", seed=57)
+    inputs = wl.generate(w)
+    hp = w.hparams()
+    log(f"case tile schedule {env}")
+    ref_out = gpu_step(inputs, "bf16", hp)
+
+    def run():
+        return gpu_step(inputs, "bf16", hp)
+
+    fn = run
+    for k, v in env.items():
+        fn = (lambda f, k, v: (lambda: _with_env(k, v, f)))(fn, k, v)
+    got = fn()
+    for i, (a, b) in enumerate(zip(ref_out, got)):
+        for name, x, y in zip(("W'", "M'", "delta"), a, b):
+            assert np.array_equal(x, y), f"matrix {i} {SHAPES[i]}: {name} differs under {env}"
