@@ -272,7 +272,9 @@ muon_status muon_dp_partition(const int64_t* sizes, const double* loads, const i
  * c_max alone forms its own group). On return order[] holds the IDs in
  * schedule order (every group a consecutive run), group_of[i] and host_of[i]
  * the group and host rank of tensor i, and *n_groups the number of groups.
- * Errors: INVALID_ARG (null pointers, n < 1, ranks outside [1, 2^20], c_max
+ * Every tentative group is solved again, as the pages do: O(n K log K) for
+ * groups of up to K tensors (milliseconds for thousands of tensors in groups
+ * of tens). Errors: INVALID_ARG (null pointers, n < 1, ranks outside [1, 2^20], c_max
  * not finite and > 0, a negative or non-finite cost). */
 muon_status muon_tp_micro_groups(const double* cost, int32_t n, int32_t ranks, double c_max, int32_t* order,
                                  int32_t* group_of, int32_t* host_of, int32_t* n_groups);

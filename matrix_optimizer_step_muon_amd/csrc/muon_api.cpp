@@ -44,8 +44,11 @@ constexpr int32_t kMaxNsSteps = 1000;
 
 }  // namespace
 
-// The error path of the other translation units (muon_partition.cpp).
-muon_status muon_fail_message(muon_status st, const char* msg) { return fail(st, msg); }
+// The error path of the other translation units (muon_partition.cpp); not
+// exported from the library.
+__attribute__((visibility("hidden"))) muon_status muon_fail_message(muon_status st, const char* msg) {
+  return fail(st, msg);
+}
 
 struct muon_plan_s {
   muon_hparams hp{};

@@ -39,7 +39,7 @@
 #pragma clang fp contract(off)
 
 // Defined in muon_api.cpp: sets this thread's error message, returns st.
-muon_status muon_fail_message(muon_status st, const char* msg);
+__attribute__((visibility("hidden"))) muon_status muon_fail_message(muon_status st, const char* msg);
 
 namespace {
 
