@@ -18,6 +18,15 @@ def _random_instance(rng):
     return R, buckets
 
 
+def test_static_rule_worked_example():
+    """The pages' Start_Index example (Canzona analysis page, section 3.4,
+    Paradigm 3) through the library: with stride S = 1,048,576, the parameter
+    starting at element 1,048,577 belongs to rank 1."""
+    S = 1_048_576
+    cuts, _ = mu.dp_partition([[S + 1, S, 2 * S - 1]], 4, alpha=None)
+    assert cuts == [[0, 1, 2, 3, 3]]
+
+
 @pytest.mark.parametrize("seed", range(60))
 def test_static_rule_matches_the_oracle(seed):
     rng = random.Random(seed)
