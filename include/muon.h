@@ -121,7 +121,12 @@ muon_status muon_plan_workspace_bytes(muon_plan_t plan, size_t* bytes);
  * synchronisation. A plan must not be stepped concurrently on two streams,
  * because its work-queue counters live in its workspace. Matrices are
  * independent, and the result does not depend on descriptor order. For a
- * fixed plan the result is bitwise deterministic. */
+ * fixed plan the result is bitwise deterministic.
+ * A step only launches kernels and records and waits on events (no memset,
+ * copy or host synchronisation; the work-queue counters are cleared by the
+ * step's own kernels), so it may be captured in a HIP graph on `stream` and
+ * the graph replayed; a replay equals an eager step bit for bit. Kernel
+ * timing (muon_plan_set_timing) must be off during capture. */
 muon_status muon_step(muon_plan_t plan, void* stream);
 
 /* Frees the plan and its workspace. NULL is a no-op. Synchronises the device. */

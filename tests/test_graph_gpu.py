@@ -1,0 +1,93 @@
+"""muon_step captured in a HIP graph (torch.cuda.graph) and replayed.
+
+A step only launches kernels and records and waits on events. It makes no
+memset, copy or host synchronisation, and it clears the work-queue counters in
+its own momentum kernels. So a caller can capture it once and replay it. This
+test checks that each replay leaves W, M and delta bit for bit equal to an
+eager step of a second plan over a copy of the same inputs. Between replays
+the program does unrelated eager work and synchronises. Bit equality is the
+bar because a plan's result does not depend on addresses or on scheduling:
+every tile sums its K steps in a fixed order.
+"""
+import time
+
+import numpy as np
+import pytest
+
+from matrix_optimizer_step_muon_amd import muon as mu
+from matrix_optimizer_step_muon_amd import workloads as wl
+
+from gpu_helpers import log, to_device, to_host
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    # bf16, two chains (the default), a ragged mix with a rank-1 matrix.
+    "bf16_ragged": ([(300, 700), (700, 300), (1, 5), (513, 512), (1024, 2048), (129, 1030)], "bf16"),
+    # bf16, the Qwen3-1.7B layer's shapes.
+    "bf16_qwen3_1p7b_layer": ([(2048, 2048), (1024, 2048), (1024, 2048), (2048, 2048), (6144, 2048),
+                               (6144, 2048), (2048, 6144)], "bf16"),
+    # fp32 engine, one chain: 16 matrices of 128 x 256.
+    "f32_tiny": ([(128, 256)] * 16, "f32"),
+}
+
+
+def _device_copy(inputs, dtype):
+    import torch
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    out = []
+    for (W, G, M) in inputs:
+        out.append([to_device(W, dtype), to_device(G, dtype), to_device(M, dtype),
+                    torch.full(W.shape, float("nan"), dtype=tdt, device="cuda")])
+    return out
+
+
+def _host(dev, dtype):
+    return [(to_host(W, dtype), to_host(M, dtype), to_host(D, dtype)) for W, _, M, D in dev]
+
+
+def _median_ms(fn, n=10):
+    import torch
+    ts = []
+    for _ in range(n):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        fn()
+        torch.cuda.synchronize()
+        ts.append((time.perf_counter() - t0) * 1e3)
+    return sorted(ts)[n // 2]
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_graph_replays_equal_eager_steps(case):
+    import torch
+    shapes, dtype = CASES[case]
+    log(f"case graph capture {case}")
+    w = wl.custom_workload(f"graph_{case}", shapes, dtype, seed=81)
+    inputs = wl.generate(w)
+    eager, graphed = _device_copy(inputs, dtype), _device_copy(inputs, dtype)
+    plan_e, plan_g = mu.Plan(eager), mu.Plan(graphed)
+    side = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        plan_g.step()                      # captured on `side`: nothing runs yet
+    torch.cuda.synchronize()
+    assert all(bool(torch.isnan(D).all()) for *_, D in graphed), "capture must not run the step"
+    x = torch.randn(512, 512, device="cuda")
+    for k in range(3):
+        plan_e.step()
+        torch.cuda.synchronize()
+        g.replay()
+        y = (x @ x).sum()                  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        assert torch.isfinite(y)
+        for i, (e, r) in enumerate(zip(_host(eager, dtype), _host(graphed, dtype))):
+            for name, a, b in zip(("W", "M", "delta"), e, r):
+                bad = np.count_nonzero(a.view(np.uint8) != b.view(np.uint8))
+                assert bad == 0, f"{case} replay {k}: matrix {i} {shapes[i]} {name}: {bad} bytes differ"
+    t_eager = _median_ms(plan_e.step)
+    t_graph = _median_ms(g.replay)
+    log(f"{case}: eager step {t_eager:.3f} ms, graph replay {t_graph:.3f} ms (host wall clock, synchronised)")
+    del g
+    plan_e.close()
+    plan_g.close()
