@@ -330,27 +330,38 @@ muon_status muon_plan(const muon_matrix* mats, int32_t n, const muon_hparams* hp
   // 4 x 4 blocks: 1.2% less step time than 4 x 8 on the Qwen3-32B layer with
   // two chains, 0.9% with one (same box; 2 x 8, 4 x 2, 2 x 4, 3 x 4, 4 x 3,
   // 4 x 6, 6 x 4 and 8 x 4 are all slower than 4 x 4).
+  // bf16 matrices of at most kSmallTileRows tile rows take kSmallBlock x
+  // kSmallBlock blocks (small_blocks); MUON_BLOCK or MUON_BLOCK_PHASES set one
+  // shape for every matrix instead.
   int brows_ph[3], bcols_ph[3], border = 1;
+  bool small_blocks = p->gemm_dtype == 1;
   for (int ph = 0; ph < 3; ++ph) { brows_ph[ph] = muon::kBlockRows; bcols_ph[ph] = muon::kBlockCols; }
   if (const char* v = std::getenv("MUON_BLOCK")) {
     int r = 0, c = 0;
-    if (std::sscanf(v, "%dx%d", &r, &c) == 2 && r > 0 && c > 0 && r * c <= 1024)
+    if (std::sscanf(v, "%dx%d", &r, &c) == 2 && r > 0 && c > 0 && r * c <= 1024) {
       for (int ph = 0; ph < 3; ++ph) { brows_ph[ph] = r; bcols_ph[ph] = c; }
+      small_blocks = false;
+    }
   }
   // MUON_BLOCK_PHASES=RxC,RxC,RxC: one shape per phase (gram, square, update).
   if (const char* v = std::getenv("MUON_BLOCK_PHASES")) {
     int r[3] = {0, 0, 0}, c[3] = {0, 0, 0};
     if (std::sscanf(v, "%dx%d,%dx%d,%dx%d", &r[0], &c[0], &r[1], &c[1], &r[2], &c[2]) == 6)
       for (int ph = 0; ph < 3; ++ph)
-        if (r[ph] > 0 && c[ph] > 0 && r[ph] * c[ph] <= 1024) { brows_ph[ph] = r[ph]; bcols_ph[ph] = c[ph]; }
+        if (r[ph] > 0 && c[ph] > 0 && r[ph] * c[ph] <= 1024) {
+          brows_ph[ph] = r[ph];
+          bcols_ph[ph] = c[ph];
+          small_blocks = false;
+        }
   }
   if (const char* v = std::getenv("MUON_BLOCK_ORDER")) border = std::atoi(v) != 0;
   for (int c = 0; c < C; ++c)
   for (int32_t i = p->chain_first[c]; i < p->chain_first[c + 1]; ++i) {
     const muon::MatDev& d = p->mats[i];
     const int32_t tm = int32_t(d.mp / T), tn = int32_t(d.np / T);
+    const bool small = small_blocks && tm <= muon::kSmallTileRows;
     for (int ph = 0; ph < 3; ++ph) {
-      const int brows = brows_ph[ph], bcols = bcols_ph[ph];
+      const int brows = small ? muon::kSmallBlock : brows_ph[ph], bcols = small ? muon::kSmallBlock : bcols_ph[ph];
       const int32_t cols = ph == muon::kUpdate ? tn : tm;
       const int64_t K = ph == muon::kGram ? d.np : d.mp;
       const int32_t nbr = (tm + brows - 1) / brows, nbc = (cols + bcols - 1) / bcols;
