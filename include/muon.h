@@ -215,7 +215,7 @@ muon_status muon_apply_plan(const muon_shard* shards, int32_t n, int32_t dtype,
  * allocation, no host synchronisation. Each sum is formed in fp32 and stored
  * once (bf16: round to nearest even), which for two values of the storage type
  * is their exactly rounded sum. Shards are independent and the result does not
- * depend on their order. */
+ * depend on their order. The call may be captured in a HIP graph on `stream`. */
 muon_status muon_apply(muon_apply_plan_t plan, void* stream);
 
 /* Frees the plan. NULL is a no-op. Synchronises the device. */

@@ -91,3 +91,36 @@ def test_graph_replays_equal_eager_steps(case):
     del g
     plan_e.close()
     plan_g.close()
+
+
+def test_graph_replays_of_the_shard_apply():
+    """muon_apply (one kernel launch) captured and replayed twice equals two
+    eager applies on a copy of the same shards, bit for bit."""
+    import torch
+    from oracle import muon_ref as ref
+    log("case graph capture shard apply")
+    r, c, ranks = 300, 700, 4
+    W = wl.to_storage(wl.draw(82, 0, 1, (r, c), 0.02), "bf16")
+    D = to_device(wl.to_storage(wl.draw(82, 0, 3, (r, c), 4e-4), "bf16"), "bf16")
+    shards = ref.tp_shard_ranges(r, c, ranks, "row")
+    sets = []
+    for _ in range(2):
+        Ps = [to_device(np.ascontiguousarray(W[rs, cs]), "bf16") for rs, cs in shards]
+        sets.append((Ps, mu.ApplyPlan([(P, D[rs, cs]) for P, (rs, cs) in zip(Ps, shards)])))
+    (Pe, plan_e), (Pg, plan_g) = sets
+    side = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        plan_g.apply()
+    torch.cuda.synchronize()
+    assert all(np.array_equal(to_host(P, "bf16"), np.ascontiguousarray(W[rs, cs])) for P, (rs, cs) in zip(Pg, shards)), \
+        "capture must not run the apply"
+    for k in range(2):
+        plan_e.apply()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(Pe, Pg)):
+            assert np.array_equal(to_host(a, "bf16"), to_host(b, "bf16")), f"replay {k}: shard {i} differs"
+    del g
+    plan_e.close()
+    plan_g.close()
