@@ -91,6 +91,7 @@ struct muon_plan_s {
     int32_t* d_qoff = nullptr;  // 3 x (kQueues + 1) queue offsets
     int32_t n_tiles[3] = {0, 0, 0};
     int32_t grid[3] = {0, 0, 0};
+    int update_variant = muon::kGemm4W;  // engine of this chain's update launches
   };
   std::vector<Chain> chains;
   std::vector<hipStream_t> aux;
@@ -210,9 +211,11 @@ muon_status muon_plan(const muon_matrix* mats, int32_t n, const muon_hparams* hp
 
   // MUON_GEMM_VARIANT=0|1|2|3 picks the bf16 engine pipeline (a tuning knob;
   // the default is the four-wave engine, 2).
+  bool variant_forced = false;
   if (const char* v = std::getenv("MUON_GEMM_VARIANT")) {
     const int k = std::atoi(v);
     p->variant = k == 0 ? muon::kGemmBK64 : k == 1 ? muon::kGemmBK32 : k == 3 ? muon::kGemm4WDeep : muon::kGemm4W;
+    variant_forced = true;
   }
   // Chains: two for the bf16 four-wave engines (MUON_CHAINS=C overrides, C in
   // [1, 8]), one otherwise; never more than there are matrices. Matrices go
@@ -355,6 +358,9 @@ muon_status muon_plan(const muon_matrix* mats, int32_t n, const muon_hparams* hp
         }
   }
   if (const char* v = std::getenv("MUON_BLOCK_ORDER")) border = std::atoi(v) != 0;
+  // Update work (tiles x K) per chain, all of it and that of matrices with at
+  // most kSmallTileRows tile rows: see update_variant below.
+  int64_t upd_all[8] = {}, upd_small[8] = {};
   for (int c = 0; c < C; ++c)
   for (int32_t i = p->chain_first[c]; i < p->chain_first[c + 1]; ++i) {
     const muon::MatDev& d = p->mats[i];
@@ -374,6 +380,10 @@ muon_status muon_plan(const muon_matrix* mats, int32_t n, const muon_hparams* hp
             if (ph == muon::kUpdate || c >= a) b.tiles.push_back({i, (a << 16) | c});
         if (b.tiles.empty()) continue;
         b.cost = int64_t(b.tiles.size()) * K;
+        if (ph == muon::kUpdate) {
+          upd_all[c] += b.cost;
+          if (tm <= muon::kSmallTileRows) upd_small[c] += b.cost;
+        }
         blocks[c][ph].push_back(std::move(b));
       }
     }
@@ -404,6 +414,18 @@ muon_status muon_plan(const muon_matrix* mats, int32_t n, const muon_hparams* hp
     }
     qo[muon::kQueues] = int32_t(tiles[c][ph].size());
     p->chains[c].n_tiles[ph] = int32_t(tiles[c][ph].size());
+    // A chain whose update work is mostly on matrices with m <= 2048 (K = m
+    // <= 2048) runs its update launches on the four-wave engine with the
+    // 4-stage ring of K step 32, which keeps three steps in flight: 4% faster
+    // on such launches, 1% slower at K = 5120 (gram and square stay on the
+    // default, which is faster for them at every size). Both engines sum each
+    // tile's 16-deep K chunks in the same order, so the results are the same
+    // bit for bit. MUON_GEMM_VARIANT sets one engine for everything.
+    if (ph == muon::kUpdate)
+      p->chains[c].update_variant = !variant_forced && p->gemm_dtype == 1 && p->variant == muon::kGemm4W &&
+                                            2 * upd_small[c] > upd_all[c]
+                                        ? muon::kGemm4WDeep
+                                        : p->variant;
     o_tiles[c][ph] = take(sizeof(muon::Tile) * std::max<size_t>(tiles[c][ph].size(), 1));
   }
   }
@@ -621,7 +643,10 @@ muon_status muon_step(muon_plan_t p, void* stream) {
                           p->d_counters + ((c * T + it) * 3 + ph) * muon::kQueues, p->d_scale, it & 1, it == 0,
                           it == T - 1, p->dtype == MUON_BF16_F32_MASTER ? 1 : 0, co};
         run_on(q, MUON_K_GRAM + ph,
-               [&] { return muon::launch_phase(p->gemm_dtype, p->variant, muon::Phase(ph), a, ch.grid[ph], q); });
+               [&] {
+                 const int v = ph == muon::kUpdate ? ch.update_variant : p->variant;
+                 return muon::launch_phase(p->gemm_dtype, v, muon::Phase(ph), a, ch.grid[ph], q);
+               });
       }
     }
   }

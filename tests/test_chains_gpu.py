@@ -82,11 +82,14 @@ def test_step_on_a_side_stream_is_joined():
 
 
 @pytest.mark.parametrize("env", [{"MUON_BLOCK": "2x8"}, {"MUON_BLOCK": "1x1", "MUON_BLOCK_ORDER": "0"},
-                                 {"MUON_BLOCK_PHASES": "4x8,2x4,8x2"}])
+                                 {"MUON_BLOCK_PHASES": "4x8,2x4,8x2"}, {"MUON_GEMM_VARIANT": "2"}])
 def test_tile_schedule_does_not_change_results(env):
     """Block shapes and the order blocks are dealt in only move tiles between
     queues and workgroups; every tile's arithmetic is the same, so the result
-    is bit for bit the default schedule's."""
+    is bit for bit the default schedule's. The same holds for the engine of the
+    update launches: these shapes (m <= 2048) update on the 4-stage engine by
+    default, and MUON_GEMM_VARIANT=2 puts them on the 2-stage one, which sums
+    the same K chunks in the same order."""
     w = wl.custom_workload("schedule", SHAPES, "bf16", seed=57)
     inputs = wl.generate(w)
     hp = w.hparams()
