@@ -414,8 +414,8 @@ muon_status muon_plan(const muon_matrix* mats, int32_t n, const muon_hparams* hp
     }
     qo[muon::kQueues] = int32_t(tiles[c][ph].size());
     p->chains[c].n_tiles[ph] = int32_t(tiles[c][ph].size());
-    // A chain whose update work is mostly on matrices with m <= 2048 (K = m
-    // <= 2048) runs its update launches on the four-wave engine with the
+    // A chain whose update work is mostly on matrices with m <= 4096 (K = m
+    // <= 4096) runs its update launches on the four-wave engine with the
     // 4-stage ring of K step 32, which keeps three steps in flight: 4% faster
     // on such launches, 1% slower at K = 5120 (gram and square stay on the
     // default, which is faster for them at every size). Both engines sum each

@@ -24,12 +24,14 @@ constexpr int kEwTile = 64;     // elementwise kernels: 64 x 64 tiles
 constexpr int kQueues = 8;
 constexpr int kBlockRows = 4;
 constexpr int kBlockCols = 4;
-// bf16 matrices with at most kSmallTileRows tile rows (m <= 2048) take blocks
-// of kSmallBlock x kSmallBlock tiles instead: their K loops are short (K = m
+// bf16 matrices with at most kSmallTileRows tile rows (m <= 4096) take blocks
+// of kSmallBlock x kSmallBlock tiles instead: their K loops are shorter (K = m
 // for square and update), and a larger block shares each operand slab among
 // more tiles. 8 x 8 measured 2.5-3% faster than 4 x 4 on batches of Qwen3-1.7B
-// shapes, while 4 x 4 stays the fastest for m = 5120.
-constexpr int kSmallTileRows = 8;
+// shapes (m = 2048), and with the update engine choice below 1-1.5% faster on
+// Qwen3-4B and 8B layer shapes (m = 2560, 4096), while 4 x 4 stays the fastest
+// for m = 5120.
+constexpr int kSmallTileRows = 16;
 constexpr int kSmallBlock = 8;
 
 // One matrix of the batch as the kernels see it. X is the m x n orientation

@@ -87,7 +87,7 @@ def test_tile_schedule_does_not_change_results(env):
     """Block shapes and the order blocks are dealt in only move tiles between
     queues and workgroups; every tile's arithmetic is the same, so the result
     is bit for bit the default schedule's. The same holds for the engine of the
-    update launches: these shapes (m <= 2048) update on the 4-stage engine by
+    update launches: these shapes (m <= 4096) update on the 4-stage engine by
     default, and MUON_GEMM_VARIANT=2 puts them on the 2-stage one, which sums
     the same K chunks in the same order."""
     w = wl.custom_workload("schedule", SHAPES, "bf16", seed=57)
