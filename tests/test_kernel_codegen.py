@@ -19,9 +19,10 @@ CSRC = os.path.join(ROOT, "matrix_optimizer_step_muon_amd", "csrc")
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 
 
-def _k_step_loops(asm: str, kernel_pattern: str, mfma_per_step: int):
-    """(kernel, loop length, MFMAs, scratch accesses) of the innermost loops of
-    the matching kernels that hold exactly one K step's MFMAs."""
+def _k_step_loops(asm: str, kernel_pattern: str, mfma_per_step: int, innermost: bool = False):
+    """(kernel, loop length, MFMAs, scratch accesses) of the loops of the
+    matching kernels that hold exactly one K step's MFMAs; with innermost, only
+    those that hold no other loop's backward branch."""
     lines = asm.split("\n")
     starts = [i for i, l in enumerate(lines) if re.match(r"^_Z\S*:", l) and re.search(kernel_pattern, l)]
     out = []
@@ -41,6 +42,11 @@ def _k_step_loops(asm: str, kernel_pattern: str, mfma_per_step: int):
             seg = body[a:i + 1]
             nm = sum(1 for x in seg if "v_mfma" in x)
             if nm != mfma_per_step:
+                continue
+            if innermost and any(re.search(r"s_(?:cbranch_\w+|branch)\s+(\.LBB\d+_\d+)", x) and
+                                 labels.get(re.search(r"(\.LBB\d+_\d+)\s*$", x.strip()).group(1), i + 1) < a + k
+                                 for k, x in enumerate(seg[:-1])
+                                 if re.search(r"s_(?:cbranch_\w+|branch)\s+\.LBB\d+_\d+\s*$", x.strip())):
                 continue
             ns = sum(1 for x in seg if re.search(r"\bscratch_(load|store)", x))
             out.append((body[0].split(":")[0], i - a, nm, ns))
@@ -67,5 +73,19 @@ def test_default_engine_k_loops_do_not_spill(kernel_asm):
     kernels = {k for k, _, _, _ in loops}
     assert len(kernels) == 5, ("expected the gram, square, update and last-update kernels (bf16 and fp32 W), "
                                f"found {kernels}")
+    bad = [(k[-40:], n, s) for k, n, _, s in loops if s]
+    assert not bad, f"K-step loops with scratch accesses (kernel, length, accesses): {bad}"
+
+
+def test_deep_update_engine_inner_k_loops_do_not_spill(kernel_asm):
+    # Engine4<true, 32, 4> (the update launches of chains of matrices with
+    # m <= 4096): K step 32 = 2 sub-steps of 16 MFMAs. Its innermost K-step
+    # loops must not spill. (Its tile loop reloads 16 accumulator registers
+    # from scratch once per tile, between the main K loop and the claim steps;
+    # the engine is measured faster than the 2-stage one on those launches
+    # with that reload.)
+    loops = _k_step_loops(kernel_asm, r"phase_kernel4INS_7Engine4ILb1ELi32ELi4EEE", 32, innermost=True)
+    kernels = {k for k, _, _, _ in loops}
+    assert len(kernels) == 3, f"expected the update and last-update kernels (bf16 and fp32 W), found {kernels}"
     bad = [(k[-40:], n, s) for k, n, _, s in loops if s]
     assert not bad, f"K-step loops with scratch accesses (kernel, length, accesses): {bad}"
