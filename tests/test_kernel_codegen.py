@@ -80,10 +80,9 @@ def test_default_engine_k_loops_do_not_spill(kernel_asm):
 def test_deep_update_engine_inner_k_loops_do_not_spill(kernel_asm):
     # Engine4<true, 32, 4> (the update launches of chains of matrices with
     # m <= 4096): K step 32 = 2 sub-steps of 16 MFMAs. Its innermost K-step
-    # loops must not spill. (Its tile loop reloads 16 accumulator registers
-    # from scratch once per tile, between the main K loop and the claim steps;
-    # the engine is measured faster than the 2-stage one on those launches
-    # with that reload.)
+    # loops must not spill. (The loop around them holds a scratch reload on
+    # the path for tiles too short to claim a successor, K < 192, which no
+    # plan takes: K is a multiple of 256.)
     loops = _k_step_loops(kernel_asm, r"phase_kernel4INS_7Engine4ILb1ELi32ELi4EEE", 32, innermost=True)
     kernels = {k for k, _, _, _ in loops}
     assert len(kernels) == 3, f"expected the update and last-update kernels (bf16 and fp32 W), found {kernels}"
