@@ -29,21 +29,37 @@ CASES = {
                                (6144, 2048), (2048, 6144)], "bf16"),
     # fp32 engine, one chain: 16 matrices of 128 x 256.
     "f32_tiny": ([(128, 256)] * 16, "f32"),
+    # fp32 master weights and momentum with bf16 gradients (MUON_BF16_F32_MASTER).
+    "master_ragged": ([(300, 700), (700, 300), (1, 5), (1024, 2048)], "master"),
 }
+
+
+def _storage(dtype):
+    """Storage types of (W, G, M, delta)."""
+    return ("f32", "bf16", "f32", "f32") if dtype == "master" else (dtype,) * 4
+
+
+def _inputs(shapes, dtype, seed):
+    if dtype != "master":
+        return wl.generate(wl.custom_workload(f"graph_{dtype}", shapes, dtype, seed=seed))
+    return [(wl.to_storage(wl.draw(seed, i, 1, s, 0.02), "f32"), wl.to_storage(wl.draw(seed, i, 0, s, 1e-3), "bf16"),
+             wl.to_storage(wl.draw(seed, i, 2, s, 1e-3), "f32")) for i, s in enumerate(shapes)]
 
 
 def _device_copy(inputs, dtype):
     import torch
-    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    sw, sg, sm, sd = _storage(dtype)
     out = []
     for (W, G, M) in inputs:
-        out.append([to_device(W, dtype), to_device(G, dtype), to_device(M, dtype),
-                    torch.full(W.shape, float("nan"), dtype=tdt, device="cuda")])
+        out.append([to_device(W, sw), to_device(G, sg), to_device(M, sm),
+                    torch.full(W.shape, float("nan"), dtype=torch.bfloat16 if sd == "bf16" else torch.float32,
+                               device="cuda")])
     return out
 
 
 def _host(dev, dtype):
-    return [(to_host(W, dtype), to_host(M, dtype), to_host(D, dtype)) for W, _, M, D in dev]
+    sw, _, sm, sd = _storage(dtype)
+    return [(to_host(W, sw), to_host(M, sm), to_host(D, sd)) for W, _, M, D in dev]
 
 
 def _median_ms(fn, n=10):
@@ -63,10 +79,11 @@ def test_graph_replays_equal_eager_steps(case):
     import torch
     shapes, dtype = CASES[case]
     log(f"case graph capture {case}")
-    w = wl.custom_workload(f"graph_{case}", shapes, dtype, seed=81)
-    inputs = wl.generate(w)
+    inputs = _inputs(shapes, dtype, 81)
     eager, graphed = _device_copy(inputs, dtype), _device_copy(inputs, dtype)
     plan_e, plan_g = mu.Plan(eager), mu.Plan(graphed)
+    if dtype == "master":
+        assert plan_g.hparams.dtype == mu.MUON_BF16_F32_MASTER
     side = torch.cuda.Stream()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=side):
