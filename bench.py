@@ -474,11 +474,10 @@ def main():
     for _ in range(args.warmup):
         plan.step(stream)
     torch.cuda.synchronize()
-    plan.reset_timing()
-    plan.set_timing(True)
 
-    # One event before the first step and one after each step: the spans
-    # give per-step times, the first-to-last span the total.
+    # The timed region: no per-kernel events, one event before the first
+    # step and one after each step. The spans give per-step times, the
+    # first-to-last span the total.
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     ev[0].record(stream)
@@ -488,8 +487,6 @@ def main():
     torch.cuda.synchronize()
     total_ms = ev[0].elapsed_time(ev[-1])
     step_ms = [ev[k].elapsed_time(ev[k + 1]) for k in range(args.steps)]
-    plan.set_timing(False)
-    ktimes = plan.kernel_times()
     ms_per_step = total_ms / args.steps
     print(f"[bench] {args.steps} steps in {total_ms:.2f} ms", file=sys.stderr, flush=True)
 
@@ -502,14 +499,14 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    # The update kernel's roofline. With two chains the update launches of
-    # one chain share the GPU with the other chain's kernels in their tails,
-    # so their durations do not measure the kernel; it is timed alone, in a
-    # separate pass over the same inputs with one chain.
-    upd_times = ktimes["update"]
-    mom_times = ktimes["momentum"]
-    upd_chains = None
-    if ktimes["update"][1] and ktimes["update"][1] // args.steps > wload.ns_steps and not args.no_roofline_pass:
+    # Per-kernel durations and the update kernel's roofline, from a separate
+    # pass of the same steps on a single-chain plan, with the library's HIP
+    # event pairs around every launch (on the stream each kernel runs on).
+    # With two chains a chain's launches share the GPU with the other chain's
+    # kernels in their tails, and their spans overlap, so they do not measure
+    # the kernels.
+    ktimes = None
+    if not args.no_roofline_pass:
         saved = os.environ.get("MUON_CHAINS")
         os.environ["MUON_CHAINS"] = "1"
         try:
@@ -528,11 +525,11 @@ def main():
             plan1.step(stream)
         torch.cuda.synchronize()
         plan1.set_timing(False)
-        kt1 = plan1.kernel_times()
-        upd_times, mom_times = kt1["update"], kt1["momentum"]
-        upd_chains = 1
+        ktimes = plan1.kernel_times()
         plan1.close()
-        print(f"[bench] roofline pass: {args.steps} single-chain steps", file=sys.stderr, flush=True)
+        print(f"[bench] per-kernel pass: {args.steps} single-chain steps", file=sys.stderr, flush=True)
+    upd_times = ktimes["update"] if ktimes else (0.0, 0)
+    mom_times = ktimes["momentum"] if ktimes else (0.0, 0)
 
     # The pages' protocol (runs x steps, each run a fresh plan), with the clock
     # sampled over its span of several seconds (the device's metrics refresh
@@ -582,8 +579,12 @@ def main():
     upd_per_step = upd_n / args.steps if upd_n else 0
     upd_flops = fl["update"] * wload.ns_steps / upd_per_step if upd_n else 0.0
     upd_tflops = upd_flops / (upd_avg / 1e3) / 1e12 if upd_n else None
-    per_kernel = {k: {"avg_ms": round(v[0] / v[1], 4), "launches": v[1],
-                      "ms_per_step": round(v[0] / args.steps, 4)} for k, v in ktimes.items() if v[1]}
+    per_kernel = None
+    if ktimes:
+        per_kernel = {k: {"avg_ms": round(v[0] / v[1], 4), "launches": v[1],
+                          "ms_per_step": round(v[0] / args.steps, 4)} for k, v in ktimes.items() if v[1]}
+        per_kernel["timed_in"] = ("a separate pass of the same steps on a single-chain plan, one HIP event "
+                                  "pair per launch; the headline steps run two chains whose launches overlap")
     elem = 2 if wload.dtype == "bf16" else 4
     # Momentum kernel algorithmic bytes: read G, M; write M' and U. A step
     # runs one momentum launch per chain (or one over all matrices); its time
@@ -631,8 +632,7 @@ def main():
             "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-scaled)",
             "alg_tflop_per_launch": round(upd_flops / 1e12, 4),
             "launches_per_step": upd_per_step,
-            "timed_in": ("a separate single-chain pass of the same steps" if upd_chains == 1
-                         else "the timed region"),
+            "timed_in": "a separate single-chain pass of the same steps",
             "avg_launch_ms": round(upd_avg, 4),
         },
         "kernels": per_kernel,

@@ -105,8 +105,9 @@ muon_status muon_hparams_default(muon_hparams* hp);
  * hp    host pointer to the hyperparameters (copied).
  * out   receives the plan handle (NULL on error).
  * Every argument is validated before any HIP call. Errors: INVALID_ARG (n < 1,
- * null pointers, rows or cols < 1, non-finite lr/beta/eps/a/b/c, beta outside
- * [0,1), eps < 0, ns_steps < 0), ALIAS, ALIGN, UNSUPPORTED (dtype). Then the
+ * null pointers, rows or cols < 1 or > 2^24 (> 2^23 for MUON_F32),
+ * non-finite lr/beta/eps/a/b/c, beta outside [0,1), eps < 0, ns_steps < 0),
+ * ALIAS, ALIGN, UNSUPPORTED (dtype). Then the
  * plan allocates and zeroes its device workspace on the current device: HIP
  * or OOM on failure. The call synchronises the device once, at its end. */
 muon_status muon_plan(const muon_matrix* mats, int32_t n, const muon_hparams* hp,

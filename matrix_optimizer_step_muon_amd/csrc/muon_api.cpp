@@ -39,7 +39,11 @@ muon_status hip_fail(hipError_t e, const char* what) {
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-constexpr int64_t kMaxDim = int64_t(1) << 24;  // tile indices are packed in 16 bits
+// Largest rows or cols. GEMM tile coordinates are packed in 16 bits each
+// (Tile::ij), so a dimension may span at most 65536 tiles: 2^24 elements with
+// the bf16 engine's 256-wide tiles, 2^23 with the fp32 engine's 128-wide ones.
+constexpr int64_t kMaxDim = int64_t(1) << 24;
+constexpr int64_t kMaxDimF32 = int64_t(65536) * muon::kTileF32;
 constexpr int32_t kMaxNsSteps = 1000;
 
 }  // namespace
@@ -63,6 +67,7 @@ struct muon_plan_s {
   std::vector<muon::MatDev> mats;  // host copy (device pointers inside)
   void* ws = nullptr;
   size_t ws_bytes = 0;
+  bool ws_owned = false;  // allocated by the plan (muon_plan), not the static scratch
 
   muon::MatDev* d_mats = nullptr;
   int32_t* d_prefix = nullptr;
@@ -157,6 +162,8 @@ muon_status validate(const muon_matrix* mats, int32_t n, const muon_hparams* hp)
     if (d.rows < 1 || d.cols < 1) return fail(MUON_ERR_INVALID_ARG, at + "rows and cols must be >= 1");
     if (d.rows > kMaxDim || d.cols > kMaxDim)
       return fail(MUON_ERR_INVALID_ARG, at + "rows and cols must be <= 2^24");
+    if (hp->dtype == MUON_F32 && (d.rows > kMaxDimF32 || d.cols > kMaxDimF32))
+      return fail(MUON_ERR_INVALID_ARG, at + "rows and cols must be <= 2^23 for MUON_F32");
     if (!d.g) return fail(MUON_ERR_INVALID_ARG, at + "g is NULL");
     if (!d.m) return fail(MUON_ERR_INVALID_ARG, at + "m is NULL");
     if (!d.w && !d.delta) return fail(MUON_ERR_INVALID_ARG, at + "w and delta are both NULL");
@@ -183,23 +190,42 @@ void free_plan(muon_plan_s* p) {
   for (auto st : p->aux) (void)hipStreamDestroy(st);
   for (auto e : p->ev_join) (void)hipEventDestroy(e);
   if (p->ev_fork) (void)hipEventDestroy(p->ev_fork);
-  if (p->ws) (void)hipFree(p->ws);
+  if (p->ws && p->ws_owned) (void)hipFree(p->ws);
   for (auto& r : p->pending) { (void)hipEventDestroy(r.start); (void)hipEventDestroy(r.end); }
   for (auto e : p->pool) (void)hipEventDestroy(e);
   delete p;
 }
 
-}  // namespace
+// Host-side tables of a plan and their places in the workspace (byte
+// offsets from its base). The plan's own fields hold the rest of the layout.
+struct PlanTables {
+  std::vector<size_t> off;  // per matrix: X ping, X pong, A, B
+  size_t o_mats = 0, o_prefix = 0, o_cprefix = 0, o_parts = 0, o_scale = 0, o_ctr = 0;
+  size_t o_qoff[8] = {};
+  size_t o_tiles[8][3] = {};
+  std::vector<int32_t> prefix, cprefix;
+  std::vector<int32_t> qoff[8];
+  std::vector<muon::Tile> tiles[8][3];
+};
 
-extern "C" {
+// One host -> device copy of a table into the workspace.
+struct Upload { void* dst; const void* src; size_t bytes; };
 
-muon_status muon_plan(const muon_matrix* mats, int32_t n, const muon_hparams* hp, muon_plan_t* out) {
-  if (!out) return fail(MUON_ERR_INVALID_ARG, "out is NULL");
-  *out = nullptr;
-  muon_status st = validate(mats, n, hp);
-  if (st != MUON_OK) return st;
-
-  auto* p = new muon_plan_s();
+// The host half of a plan: orientation, padding, chains, LPT tile tables and
+// the workspace layout (p->ws_bytes). No HIP call. one_chain: a single chain
+// whatever the tuning knobs say (the no-allocation step has no second
+// stream). Arguments are validated by the caller.
+muon_status plan_host(const muon_matrix* mats, int32_t n, const muon_hparams* hp, bool one_chain, muon_plan_s* p,
+                      PlanTables& t) {
+  std::vector<size_t>& off = t.off;
+  std::vector<int32_t>& prefix = t.prefix;
+  std::vector<int32_t>& cprefix = t.cprefix;
+  size_t &o_mats = t.o_mats, &o_prefix = t.o_prefix, &o_cprefix = t.o_cprefix, &o_parts = t.o_parts,
+         &o_scale = t.o_scale, &o_ctr = t.o_ctr;
+  auto& o_qoff = t.o_qoff;
+  auto& o_tiles = t.o_tiles;
+  auto& qoff = t.qoff;
+  auto& tiles = t.tiles;
   p->hp = *hp;
   p->dtype = hp->dtype;
   // Newton-Schulz runs in bf16 for MUON_BF16 and MUON_BF16_F32_MASTER.
@@ -221,13 +247,12 @@ muon_status muon_plan(const muon_matrix* mats, int32_t n, const muon_hparams* hp
   // [1, 8]), one otherwise; never more than there are matrices. Matrices go
   // largest first (multiply-adds of one iteration) to the lightest chain.
   const bool four_wave = p->variant == muon::kGemm4W || p->variant == muon::kGemm4WDeep;
-  if (p->dtype == MUON_BF16_F32_MASTER && !four_wave) {
-    free_plan(p);
+  if (p->dtype == MUON_BF16_F32_MASTER && !four_wave)
     return fail(MUON_ERR_UNSUPPORTED, "MUON_BF16_F32_MASTER needs the four-wave GEMM engine (MUON_GEMM_VARIANT 2 or 3)");
-  }
   int C = (p->gemm_dtype == 1 && four_wave) ? 2 : 1;
   if (const char* v = std::getenv("MUON_CHAINS")) C = std::max(1, std::min(8, std::atoi(v)));
   C = std::min<int>(C, n);
+  if (one_chain) C = 1;
   std::vector<std::vector<int32_t>> members(C);
   {
     std::vector<std::pair<int64_t, int32_t>> wts(n);
@@ -261,10 +286,10 @@ muon_status muon_plan(const muon_matrix* mats, int32_t n, const muon_hparams* hp
 
   // Orientation, padding and workspace offsets.
   p->mats.resize(n);
-  std::vector<size_t> off(n * 4);
+  off.assign(size_t(n) * 4, 0);
   size_t cursor = 0;
   auto take = [&](size_t bytes) { size_t o = cursor; cursor = round_up(cursor + bytes, 256); return o; };
-  std::vector<int32_t> prefix(n + 1, 0);
+  prefix.assign(n + 1, 0);
   int32_t parts = 0;
   for (int32_t i = 0; i < n; ++i) {
     const muon_matrix& s = mats[order[i]];
@@ -302,21 +327,21 @@ muon_status muon_plan(const muon_matrix* mats, int32_t n, const muon_hparams* hp
     off[i * 4 + 3] = take(abytes);
   }
   p->ew_blocks = prefix[n];
-  std::vector<int32_t> cprefix(n + C, 0);
+  cprefix.assign(n + C, 0);
   p->chain_ew_blocks.assign(C, 0);
   for (int c = 0; c < C; ++c) {
     const int32_t f = p->chain_first[c], base = f + c;
     for (int32_t i = f; i < p->chain_first[c + 1]; ++i) cprefix[base + (i - f) + 1] = cprefix[base + (i - f)] + (prefix[i + 1] - prefix[i]);
     p->chain_ew_blocks[c] = prefix[p->chain_first[c + 1]] - prefix[f];
   }
-  const size_t o_mats = take(sizeof(muon::MatDev) * n);
-  const size_t o_prefix = take(sizeof(int32_t) * (n + 1));
-  const size_t o_cprefix = take(sizeof(int32_t) * (n + C));
-  const size_t o_parts = take(sizeof(float) * std::max(parts, 1));
-  const size_t o_scale = take(sizeof(float) * n);
+  o_mats = take(sizeof(muon::MatDev) * n);
+  o_prefix = take(sizeof(int32_t) * (n + 1));
+  o_cprefix = take(sizeof(int32_t) * (n + C));
+  o_parts = take(sizeof(float) * std::max(parts, 1));
+  o_scale = take(sizeof(float) * n);
   p->chains.resize(C);
   p->n_counters = std::max(C * 3 * hp->ns_steps * muon::kQueues, 1);
-  const size_t o_ctr = take(sizeof(int32_t) * p->n_counters);
+  o_ctr = take(sizeof(int32_t) * p->n_counters);
 
   // Tile tables. Each phase's tiles are cut into blocks of kBlockRows x
   // kBlockCols tiles of one matrix. Blocks are dealt longest first to the
@@ -388,10 +413,6 @@ muon_status muon_plan(const muon_matrix* mats, int32_t n, const muon_hparams* hp
       }
     }
   }
-  size_t o_tiles[8][3];
-  size_t o_qoff[8];
-  std::vector<muon::Tile> tiles[8][3];
-  std::vector<int32_t> qoff[8];
   for (int c = 0; c < C; ++c) {
   o_qoff[c] = take(sizeof(int32_t) * 3 * (muon::kQueues + 1));
   qoff[c].assign(3 * (muon::kQueues + 1), 0);
@@ -430,16 +451,75 @@ muon_status muon_plan(const muon_matrix* mats, int32_t n, const muon_hparams* hp
   }
   }
   p->ws_bytes = cursor;
+  return MUON_OK;
+}
 
-  // ---- HIP from here on.
+// Device facts of a plan on the current device: the device and the
+// persistent grid of every GEMM launch (one workgroup per resident slot).
+muon_status plan_device(muon_plan_s* p) {
   hipError_t e = hipGetDevice(&p->device);
-  if (e != hipSuccess) { free_plan(p); return hip_fail(e, "hipGetDevice"); }
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
   int n_cu = 0;
   e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, p->device);
-  if (e != hipSuccess) { free_plan(p); return hip_fail(e, "hipDeviceGetAttribute"); }
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
   const int32_t resident = n_cu * muon::gemm_blocks_per_cu(p->gemm_dtype, p->variant);
   for (auto& ch : p->chains)
     for (int ph = 0; ph < 3; ++ph) ch.grid[ph] = std::max(1, std::min(ch.n_tiles[ph], resident));
+  return MUON_OK;
+}
+
+// Points the plan at a workspace at `base` (ws_bytes long) and lists the
+// table copies that fill it. The host tables must outlive the copies.
+std::vector<Upload> plan_bind(muon_plan_s* p, const PlanTables& t, char* base) {
+  p->ws = base;
+  const int32_t n = p->n, C = int32_t(p->chains.size());
+  for (int32_t i = 0; i < n; ++i) {
+    muon::MatDev& d = p->mats[i];
+    d.x[0] = base + t.off[i * 4 + 0];
+    d.x[1] = base + t.off[i * 4 + 1];
+    d.a = base + t.off[i * 4 + 2];
+    d.b = base + t.off[i * 4 + 3];
+  }
+  p->d_mats = reinterpret_cast<muon::MatDev*>(base + t.o_mats);
+  p->d_prefix = reinterpret_cast<int32_t*>(base + t.o_prefix);
+  p->d_cprefix = reinterpret_cast<int32_t*>(base + t.o_cprefix);
+  p->d_partials = reinterpret_cast<float*>(base + t.o_parts);
+  p->d_scale = reinterpret_cast<float*>(base + t.o_scale);
+  p->d_counters = reinterpret_cast<int32_t*>(base + t.o_ctr);
+  std::vector<Upload> ups = {
+      {p->d_mats, p->mats.data(), sizeof(muon::MatDev) * n},
+      {p->d_prefix, t.prefix.data(), sizeof(int32_t) * (n + 1)},
+      {p->d_cprefix, t.cprefix.data(), sizeof(int32_t) * t.cprefix.size()},
+  };
+  for (int c = 0; c < C; ++c) {
+    muon_plan_s::Chain& ch = p->chains[c];
+    ch.d_qoff = reinterpret_cast<int32_t*>(base + t.o_qoff[c]);
+    ups.push_back({ch.d_qoff, t.qoff[c].data(), sizeof(int32_t) * t.qoff[c].size()});
+    for (int ph = 0; ph < 3; ++ph) {
+      ch.d_tiles[ph] = reinterpret_cast<muon::Tile*>(base + t.o_tiles[c][ph]);
+      ups.push_back({ch.d_tiles[ph], t.tiles[c][ph].data(), sizeof(muon::Tile) * t.tiles[c][ph].size()});
+    }
+  }
+  return ups;
+}
+
+}  // namespace
+
+extern "C" {
+
+muon_status muon_plan(const muon_matrix* mats, int32_t n, const muon_hparams* hp, muon_plan_t* out) {
+  if (!out) return fail(MUON_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  muon_status st = validate(mats, n, hp);
+  if (st != MUON_OK) return st;
+
+  auto* p = new muon_plan_s();
+  PlanTables t;
+  st = plan_host(mats, n, hp, false, p, t);
+  if (st == MUON_OK) st = plan_device(p);
+  if (st != MUON_OK) { free_plan(p); return st; }
+  const int C = int(p->chains.size());
+  hipError_t e = hipSuccess;
   // Auxiliary streams (default priority, not synchronising with the null
   // stream) and the fork / join events of the chains.
   for (int c = 1; c < C; ++c) {
@@ -457,45 +537,19 @@ muon_status muon_plan(const muon_matrix* mats, int32_t n, const muon_hparams* hp
     if (e != hipSuccess) { free_plan(p); return hip_fail(e, "hipEventCreateWithFlags"); }
   }
 
-  e = hipMalloc(&p->ws, p->ws_bytes);
+  void* ws = nullptr;
+  e = hipMalloc(&ws, p->ws_bytes);
   if (e != hipSuccess) {
-    p->ws = nullptr;
     free_plan(p);
     (void)hipGetLastError();
     return fail(MUON_ERR_OOM, "hipMalloc of " + std::to_string(p->ws_bytes) + " workspace bytes failed");
   }
-  char* base = static_cast<char*>(p->ws);
+  p->ws = ws;
+  p->ws_owned = true;
   e = hipMemset(p->ws, 0, p->ws_bytes);
   if (e != hipSuccess) { free_plan(p); return hip_fail(e, "hipMemset"); }
-  for (int32_t i = 0; i < n; ++i) {
-    muon::MatDev& d = p->mats[i];
-    d.x[0] = base + off[i * 4 + 0];
-    d.x[1] = base + off[i * 4 + 1];
-    d.a = base + off[i * 4 + 2];
-    d.b = base + off[i * 4 + 3];
-  }
-  p->d_mats = reinterpret_cast<muon::MatDev*>(base + o_mats);
-  p->d_prefix = reinterpret_cast<int32_t*>(base + o_prefix);
-  p->d_cprefix = reinterpret_cast<int32_t*>(base + o_cprefix);
-  p->d_partials = reinterpret_cast<float*>(base + o_parts);
-  p->d_scale = reinterpret_cast<float*>(base + o_scale);
-  p->d_counters = reinterpret_cast<int32_t*>(base + o_ctr);
-  struct Up { void* dst; const void* src; size_t bytes; };
-  std::vector<Up> ups = {
-      {p->d_mats, p->mats.data(), sizeof(muon::MatDev) * n},
-      {p->d_prefix, prefix.data(), sizeof(int32_t) * (n + 1)},
-      {p->d_cprefix, cprefix.data(), sizeof(int32_t) * cprefix.size()},
-  };
-  for (int c = 0; c < C; ++c) {
-    muon_plan_s::Chain& ch = p->chains[c];
-    ch.d_qoff = reinterpret_cast<int32_t*>(base + o_qoff[c]);
-    ups.push_back({ch.d_qoff, qoff[c].data(), sizeof(int32_t) * qoff[c].size()});
-    for (int ph = 0; ph < 3; ++ph) {
-      ch.d_tiles[ph] = reinterpret_cast<muon::Tile*>(base + o_tiles[c][ph]);
-      ups.push_back({ch.d_tiles[ph], tiles[c][ph].data(), sizeof(muon::Tile) * tiles[c][ph].size()});
-    }
-  }
-  for (const Up& u : ups) {
+  const std::vector<Upload> ups = plan_bind(p, t, static_cast<char*>(ws));
+  for (const Upload& u : ups) {
     if (u.bytes == 0) continue;
     e = hipMemcpy(u.dst, u.src, u.bytes, hipMemcpyHostToDevice);
     if (e != hipSuccess) { free_plan(p); return hip_fail(e, "hipMemcpy"); }

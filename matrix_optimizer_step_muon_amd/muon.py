@@ -164,6 +164,36 @@ def plan(mats: Iterable[Sequence], *, dtype: Optional[int] = None, **hparams) ->
     return p
 
 
+def _descriptors(mats: Iterable[Sequence]):
+    """Descriptors of a batch of ``(W, G, M[, delta])`` device tensors, the
+    batch's dtype code and the tensors themselves."""
+    tensors: List = []
+    descs = []
+    dtype = None
+    for entry in mats:
+        W, G, M = entry[0], entry[1], entry[2]
+        D = entry[3] if len(entry) > 3 else None
+        ref = W if W is not None else D
+        for t in (W, G, M, D):
+            if t is None:
+                continue
+            if not t.is_cuda or not t.is_contiguous() or t.dim() != 2:
+                raise MuonError(-1, "tensors must be contiguous 2-D device tensors")
+            if tuple(t.shape) != tuple(ref.shape):
+                raise MuonError(-1, "the tensors of a matrix must share one shape")
+        code = _batch_dtype(W, G, M, D)
+        if dtype is not None and code != dtype:
+            raise MuonError(-1, "every matrix of a batch must have the same dtypes")
+        dtype = code
+        tensors.append((W, G, M, D))
+        descs.append(muon_matrix(W.data_ptr() if W is not None else None, G.data_ptr(),
+                                 M.data_ptr(), D.data_ptr() if D is not None else None,
+                                 ref.shape[0], ref.shape[1]))
+    if not descs:
+        raise MuonError(-1, "empty batch")
+    return descs, dtype, tensors
+
+
 class Plan:
     """A static plan over a batch of ``(W, G, M[, delta])`` device tensors.
 
@@ -175,30 +205,7 @@ class Plan:
     def __init__(self, mats: Iterable[Sequence], *, lr=0.02, beta=0.95, eps=1e-7,
                  coeffs=(3.4445, -4.7750, 2.0315), ns_steps=5, nesterov=True):
         self._handle = None
-        self._tensors: List = []
-        descs = []
-        dtype = None
-        for entry in mats:
-            W, G, M = entry[0], entry[1], entry[2]
-            D = entry[3] if len(entry) > 3 else None
-            ref = W if W is not None else D
-            for t in (W, G, M, D):
-                if t is None:
-                    continue
-                if not t.is_cuda or not t.is_contiguous() or t.dim() != 2:
-                    raise MuonError(-1, "tensors must be contiguous 2-D device tensors")
-                if tuple(t.shape) != tuple(ref.shape):
-                    raise MuonError(-1, "the tensors of a matrix must share one shape")
-            code = _batch_dtype(W, G, M, D)
-            if dtype is not None and code != dtype:
-                raise MuonError(-1, "every matrix of a batch must have the same dtypes")
-            dtype = code
-            self._tensors.append((W, G, M, D))
-            descs.append(muon_matrix(W.data_ptr() if W is not None else None, G.data_ptr(),
-                                     M.data_ptr(), D.data_ptr() if D is not None else None,
-                                     ref.shape[0], ref.shape[1]))
-        if not descs:
-            raise MuonError(-1, "empty batch")
+        descs, dtype, self._tensors = _descriptors(mats)
         self.hparams = make_hparams(lr, beta, eps, coeffs, ns_steps, nesterov, dtype)
         self._handle = plan_raw(descs, self.hparams)
 

@@ -12,7 +12,6 @@ from .muon_ref import (  # noqa: F401
     frobenius_normalize,
     momentum_update,
     muon_step,
-    muon_step_batch,
     newton_schulz,
     orthogonalize,
     step_flops,

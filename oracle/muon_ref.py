@@ -147,13 +147,6 @@ def muon_step(W: np.ndarray, G: np.ndarray, M: np.ndarray, *, lr: float,
     return W_new, M_new, O
 
 
-def muon_step_batch(mats, **hp):
-    """The step over a list of ``(W, G, M)``. The matrices are independent of
-    one another, as each owned tensor is updated locally with no communication
-    (Canzona analysis page, section 3.4, DP per-iteration execution, phase 2)."""
-    return [muon_step(W, G, M, **hp) for (W, G, M) in mats]
-
-
 def step_flops(rows: int, cols: int, ns_steps: int = DEFAULT_NS_STEPS) -> int:
     """Algorithmic flops of the Newton-Schulz part of one step on one matrix.
 

@@ -14,6 +14,10 @@ from oracle import muon_ref as ref
 
 TOL = {"bf16": 2e-2, "f32": 1e-4}
 
+# Every comparison made in this session: (label, shape, {"O": .., "M": .., "W": ..},
+# tolerance, full_size). tests/conftest.py prints them at the end of the run.
+RECORDS = []
+
 
 def log(msg: str) -> None:
     print(f"[{time.strftime('%H:%M:%S')}] {msg}", flush=True)
@@ -74,9 +78,11 @@ def oracle_step(inputs, dtype: str, hp: dict, steps=1, grads=None):
     return res
 
 
-def compare(gpu, want, dtype: str, hp: dict, inputs, label: str, tol=None):
+def compare(gpu, want, dtype: str, hp: dict, inputs, label: str, tol=None, full_size=False):
     """relFro of O (from delta), M' and W' against the oracle, per matrix.
-    Returns the worst of each and asserts them against the tolerance."""
+    Returns the worst of each and asserts them against the tolerance. Every
+    result is also recorded in RECORDS (full_size marks the full-size cases,
+    which the end-of-run summary lists matrix by matrix)."""
     tol = TOL[dtype] if tol is None else tol
     worst = {"O": 0.0, "M": 0.0, "W": 0.0}
     for i, ((Wg, Mg, Dg), (Wr, Mr, Or)) in enumerate(zip(gpu, want)):
@@ -91,6 +97,7 @@ def compare(gpu, want, dtype: str, hp: dict, inputs, label: str, tol=None):
             errs["W"] = wl.rel_fro(wl.stored_to_f64(Wg, dtype), Wr)
         for k, v in errs.items():
             worst[k] = max(worst[k], v)
+        RECORDS.append((label, (r, c), dict(errs), tol, full_size))
         log(f"{label} matrix {i} {r}x{c}: " + " ".join(f"relFro({k})={v:.3e}" for k, v in errs.items()))
         for k, v in errs.items():
             assert v <= tol, f"{label} matrix {i} ({r}x{c}): relFro({k}) = {v:.3e} > {tol}"

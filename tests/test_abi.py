@@ -87,6 +87,7 @@ def plan_status(descs, hp=None, n=None):
     ("alias_within", -2, "overlaps"),
     ("alias_across", -2, "overlaps"),
     ("too_big", -1, "2^24"),
+    ("too_big_f32", -1, "2^23"),
 ])
 def test_plan_validation(case, status, msg):
     d = [desc(0), desc(1)]
@@ -128,6 +129,11 @@ def test_plan_validation(case, status, msg):
         d[1].w = d[0].w + 128
     elif case == "too_big":
         d[0].cols = (1 << 24) + 1
+    elif case == "too_big_f32":
+        # fp32 tiles are 128 wide and tile coordinates 16 bits: 2^23 + 128
+        # columns would need tile column 65536.
+        hp.dtype = muon.MUON_F32
+        d[0].rows, d[0].cols = 1, (1 << 23) + 128
     st, out, err = plan_status(d, hp, n)
     assert st == status, err
     assert msg in err
@@ -306,3 +312,4 @@ def test_master_weights_need_the_four_wave_engine(monkeypatch):
     hp = muon.make_hparams(dtype=muon.MUON_BF16_F32_MASTER)
     st, out, err = plan_status([desc(0, elem=4)], hp)
     assert st == -4 and "four-wave" in err and out is None
+

@@ -5,10 +5,15 @@ bf16 path, checked on:
 - O, recovered from the delta output;
 - the momentum buffer M';
 - the weights W'.
-Sizes span several tiles and ragged tails. The last test runs the full
-Qwen3-32B layer in the same plan and launch configuration that bench.py times,
-and checks sampled matrices and properties that hold at any size.
+Sizes span several tiles and ragged tails. The full-size cases run the
+Qwen3-32B layer, the 28 Qwen3-1.7B layers and the Qwen3-32B rank share in the
+plan and launch configuration that bench.py times: every matrix of the
+Qwen3-32B layer, and one or more of every shape of the other two, are compared
+with the oracle in full, and properties that hold at any size are checked on
+every matrix.
 """
+
+import functools
 
 import numpy as np
 import pytest
@@ -140,29 +145,48 @@ def test_delta_only_mode_leaves_no_weight_write():
     compare(gpu, want, "bf16", hp, inputs, "delta only")
 
 
-def full_size_sampled(name, sample):
-    """One full-size workload in one plan, as bench.py would time it.
+# Full-size workloads, in the plan and launch configuration bench.py times.
+# Each workload's HIP step runs once (the first case that needs it) and its
+# outputs are kept while that workload's cases run; every listed matrix is then
+# compared with the oracle in full, one case per matrix, so that no case runs
+# for long. Per workload:
+# - the Qwen3-32B layer: all seven matrices (q, k, v, o, gate, up, down);
+# - the 28 Qwen3-1.7B layers: one matrix of each of the seven shapes, taken
+#   from seven different layers;
+# - the Qwen3-32B rank share: layer 1's q, o and down, the two extra
+#   1024 x 5120 matrices and the extra 25600 x 5120 one.
+# A last case per workload checks properties that hold at any size on every
+# matrix of the batch.
+FULL_ORACLE = {
+    "qwen3_32b_layer": list(range(7)),
+    "qwen3_1p7b_28_layers": [0, 7 * 5 + 1, 7 * 10 + 2, 7 * 14 + 3, 7 * 19 + 4, 7 * 23 + 5, 7 * 27 + 6],
+    "qwen3_32b_rank_share": [7, 10, 13, 14, 15, 16],
+}
+FULL_CASES = [(name, i) for name, idx in FULL_ORACLE.items() for i in idx + [None]]
 
-    Checked here:
-    - the matrices in `sample` against the oracle in full;
-    - M' of every matrix on 20000 sampled elements against the elementwise
-      definition;
-    - W' + delta consistency everywhere;
-    - for every matrix, the Gram matrix of O has eigenvalues in the square of
-      the quintic's reachable interval. Square Gaussian matrices have smallest
-      singular values near 0, which five steps do not lift into the band, so
-      for them only the upper bound is checked.
-    """
-    import torch
+
+@functools.lru_cache(maxsize=1)
+def _full_run(name):
+    """(inputs, HIP outputs) of one full-size workload; one workload is held
+    at a time."""
     wload = wl.WORKLOADS[name]
-    hp = wload.hparams()
     log(f"case {name}: generating inputs ({len(wload.shapes)} matrices, {wload.numel / 1e6:.0f} M elements)")
     inputs = wl.generate(wload)
     log(f"case {name}: running the HIP step")
-    gpu = gpu_step(inputs, "bf16", hp)
-    log(f"case {name}: oracle on matrices {sample}")
-    want = oracle_step([inputs[i] for i in sample], "bf16", hp)
-    compare([gpu[i] for i in sample], want, "bf16", hp, [inputs[i] for i in sample], f"{name} sample")
+    gpu = gpu_step(inputs, "bf16", wload.hparams())
+    return inputs, gpu
+
+
+def _full_size_properties(name, inputs, gpu, hp):
+    """On every matrix of the batch:
+    - M' on 20000 sampled elements against the elementwise definition;
+    - W' against W + delta everywhere (each is rounded once from one fp32
+      update);
+    - the singular values of O within the quintic's reachable interval after
+      five steps. Square Gaussian matrices have smallest singular values near
+      0, which five steps do not lift into the band, so for them only the
+      upper bound is checked."""
+    import torch
     rng = np.random.default_rng(0)
     lo, top = 0.681831, 1.202369
     for i, ((W, G, M), (Wg, Mg, Dg)) in enumerate(zip(inputs, gpu)):
@@ -185,18 +209,19 @@ def full_size_sampled(name, sample):
             assert sv.min() > lo * 0.97, f"{name} matrix {i} ({r}x{c}): sigma_min {sv.min()}"
 
 
-def test_qwen3_32b_layer_full_size_sampled():
-    """Qwen3-32B layer: k and v (1024 x 5120) against the oracle."""
-    full_size_sampled("qwen3_32b_layer", [1, 2])
-
-
-def test_qwen3_1p7b_28_layers_full_size_sampled():
-    """All 196 matrices of the Qwen3-1.7B shapes in one step: layer 0's k and
-    the last layer's gate (6144 x 2048) against the oracle."""
-    full_size_sampled("qwen3_1p7b_28_layers", [1, 27 * 7 + 4])
-
-
-def test_qwen3_32b_rank_share_full_size_sampled():
-    """One rank's share (17 matrices): the two extra 1024 x 5120 matrices
-    against the oracle."""
-    full_size_sampled("qwen3_32b_rank_share", [14, 15])
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,index", FULL_CASES,
+                         ids=[f"{n}-{'properties' if i is None else i}" for n, i in FULL_CASES])
+def test_full_size_against_oracle(name, index):
+    """One matrix of a full-size workload against the oracle on O, M' and W'
+    (index None: the properties above, on every matrix)."""
+    wload = wl.WORKLOADS[name]
+    hp = wload.hparams()
+    inputs, gpu = _full_run(name)
+    if index is None:
+        _full_size_properties(name, inputs, gpu, hp)
+        return
+    r, c = wload.shapes[index]
+    log(f"case {name}: oracle on matrix {index} ({r}x{c})")
+    want = oracle_step([inputs[index]], "bf16", hp)
+    compare([gpu[index]], want, "bf16", hp, [inputs[index]], f"{name} full size #{index}", full_size=True)
