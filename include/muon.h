@@ -133,6 +133,33 @@ muon_status muon_step(muon_plan_t plan, void* stream);
 /* Frees the plan and its workspace. NULL is a no-op. Synchronises the device. */
 muon_status muon_plan_destroy(muon_plan_t plan);
 
+/* Bytes of the static device scratch that muon_step_noalloc works in. */
+#define MUON_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* One step that allocates nothing, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc. It computes what muon_plan, one muon_step and
+ * muon_plan_destroy compute, bit for bit, but keeps its workspace (the
+ * Newton-Schulz buffers, norm partials, work-queue counters and tile tables)
+ * in a static device array of MUON_NOALLOC_SCRATCH_BYTES (64 MiB), one per
+ * GPU, which the library holds from its first use on that GPU until the
+ * process ends. It calls no hipMalloc or hipFree and creates no stream or
+ * event: everything is enqueued on `stream` (a hipStream_t; NULL is the null
+ * stream) as one chain of launches: a fill kernel clears the workspace,
+ * small kernels copy the tables in (their bytes travel as kernel arguments),
+ * then the step's kernels run. Host-side bookkeeping (building the tables) uses
+ * ordinary host memory.
+ * mats, n, hp: as for muon_plan (the same validation and errors), device
+ * pointers on the current device. The tensors must stay valid until the step
+ * has run on the stream.
+ * Errors: those of muon_plan's validation; INVALID_ARG if the batch's
+ * workspace exceeds the scratch (the message gives both sizes); HIP.
+ * Every call on a GPU works in that GPU's one array, which keeps the last
+ * call's contents: calls that overlap on one GPU (on two streams without an
+ * ordering between them, or from two threads) race and give wrong results.
+ * Calls issued one after another on one stream are safe. */
+muon_status muon_step_noalloc(const muon_matrix* mats, int32_t n, const muon_hparams* hp, void* stream);
+
 /* This thread's last error message ("" if none). Valid until this thread's
  * next call into the library. */
 const char* muon_last_error(void);

@@ -714,6 +714,37 @@ muon_status muon_step(muon_plan_t p, void* stream) {
   return st;
 }
 
+muon_status muon_step_noalloc(const muon_matrix* mats, int32_t n, const muon_hparams* hp, void* stream) {
+  muon_status st = validate(mats, n, hp);
+  if (st != MUON_OK) return st;
+  auto* p = new muon_plan_s();
+  PlanTables t;
+  st = plan_host(mats, n, hp, true, p, t);
+  if (st == MUON_OK && p->ws_bytes > muon::kScratchBytes)
+    st = fail(MUON_ERR_INVALID_ARG, "the batch needs " + std::to_string(p->ws_bytes) +
+                                        " workspace bytes, more than the " + std::to_string(muon::kScratchBytes) +
+                                        " bytes of static scratch; use muon_plan");
+  if (st == MUON_OK) st = plan_device(p);
+  void* base = nullptr;
+  if (st == MUON_OK) {
+    const hipError_t e = muon::scratch_address(&base);
+    if (e != hipSuccess) st = hip_fail(e, "hipGetSymbolAddress");
+  }
+  if (st != MUON_OK) { free_plan(p); return st; }
+  // The previous call's contents are still in the array: clear the
+  // workspace (the X buffers' padding must read as zero), copy the tables
+  // in, and run the step, all on `stream`.
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const std::vector<Upload> ups = plan_bind(p, t, static_cast<char*>(base));
+  hipError_t e = muon::launch_zero(base, p->ws_bytes, s);
+  for (size_t k = 0; e == hipSuccess && k < ups.size(); ++k)
+    e = muon::launch_upload(ups[k].dst, ups[k].src, ups[k].bytes, s);
+  if (e != hipSuccess) st = hip_fail(e, "kernel launch");
+  if (st == MUON_OK) st = muon_step(p, stream);
+  free_plan(p);  // host tables only: the workspace is the static array
+  return st;
+}
+
 muon_status muon_plan_destroy(muon_plan_t p) {
   if (!p) return MUON_OK;
   hipError_t e = hipDeviceSynchronize();

@@ -131,4 +131,16 @@ hipError_t launch_phase(int dtype, int variant, Phase ph, const PhaseArgs& args,
 // Workgroups per CU that the persistent GEMM kernels can keep resident.
 int gemm_blocks_per_cu(int dtype, int variant);
 
+// The no-allocation step's workspace: a static device array of kScratchBytes
+// per GPU (muon_kernels.hip). scratch_address() gives its device address on
+// the current device, looked up once per device.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+hipError_t scratch_address(void** out);
+// dst[0 .. bytes) = 0 (bytes a multiple of 16, dst 16-byte aligned).
+hipError_t launch_zero(void* dst, size_t bytes, hipStream_t s);
+// Copies bytes from host src to device dst by kernel launches that carry the
+// data in their arguments (dst 16-byte aligned; the copy is rounded up to 16
+// bytes, so up to 15 bytes past dst + bytes are written with zeros).
+hipError_t launch_upload(void* dst, const void* src, size_t bytes, hipStream_t s);
+
 }  // namespace muon

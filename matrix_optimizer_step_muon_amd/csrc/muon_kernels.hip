@@ -31,6 +31,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+#include <cstring>
+#include <mutex>
 #include <type_traits>
 
 #include "muon_internal.h"
@@ -2056,6 +2059,79 @@ __global__ void __launch_bounds__(256) mfma_probe_kernel(float* out, int iters) 
 #pragma unroll
     for (int e = 0; e < 16; ++e) sum += acc[j][e];
   out[(size_t)blockIdx.x * 256 + tid] = sum;
+}
+
+// ------------------------------------------------------------ static scratch
+//
+// The workspace of muon_step_noalloc: one array per GPU, held by the library
+// from its first use on that GPU until the process ends. Host code never uses
+// the array's name as an address (on the host it names a stand-in, not device
+// memory): scratch_address() looks up the device address once per device,
+// with that device current, and every later use goes through that pointer.
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+hipError_t scratch_address(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* ptrs[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    ptrs[dev] = p;
+  }
+  *out = ptrs[dev];
+  return hipSuccess;
+}
+
+// dst[0 .. n16) = 0 in 16-byte words (grid-stride).
+__global__ void __launch_bounds__(256) zero_kernel(u32x4* dst, int64_t n16) {
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (int64_t)gridDim.x * 256)
+    *((g_u32x4*)(dst + i)) = z;
+}
+
+// A table copy whose bytes travel in the kernel arguments, so the host
+// buffer they came from may be freed as soon as the launch returns.
+constexpr int kUploadWords = 120;  // 16-byte words per launch
+struct UploadArgs {
+  u32x4* dst;
+  int32_t n16;
+  u32x4 words[kUploadWords];
+};
+__global__ void __launch_bounds__(128) upload_kernel(UploadArgs a) {
+  if ((int)threadIdx.x < a.n16) *((g_u32x4*)(a.dst + threadIdx.x)) = a.words[threadIdx.x];
+}
+
+hipError_t launch_zero(void* dst, size_t bytes, hipStream_t s) {
+  const int64_t n16 = (int64_t)(bytes / 16);
+  if (n16 == 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((n16 + 255) / 256, 4096);
+  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s, static_cast<u32x4*>(dst), n16);
+  return hipGetLastError();
+}
+
+hipError_t launch_upload(void* dst, const void* src, size_t bytes, hipStream_t s) {
+  const unsigned char* in = static_cast<const unsigned char*>(src);
+  unsigned char* out = static_cast<unsigned char*>(dst);
+  for (size_t done = 0; done < bytes; done += 16 * kUploadWords) {
+    const size_t len = std::min<size_t>(bytes - done, 16 * kUploadWords);
+    UploadArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.dst = reinterpret_cast<u32x4*>(out + done);
+    a.n16 = (int32_t)((len + 15) / 16);
+    std::memcpy(a.words, in + done, len);
+    hipLaunchKernelGGL(upload_kernel, dim3(1), dim3(128), 0, s, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 // ------------------------------------------------------------ launchers

@@ -52,7 +52,8 @@ EXPORTS = ("muon_hparams_default", "muon_plan", "muon_plan_workspace_bytes", "mu
            "muon_plan_destroy", "muon_last_error", "muon_plan_set_timing",
            "muon_plan_kernel_times", "muon_plan_reset_timing", "muon_plan_info",
            "muon_apply_plan", "muon_apply", "muon_apply_plan_destroy",
-           "muon_dp_partition_static", "muon_dp_partition", "muon_tp_micro_groups", "muon_mfma_probe")
+           "muon_dp_partition_static", "muon_dp_partition", "muon_tp_micro_groups", "muon_mfma_probe",
+           "muon_step_noalloc")
 
 
 def lib() -> ctypes.CDLL:
@@ -84,6 +85,7 @@ def lib() -> ctypes.CDLL:
     L.muon_dp_partition_static.argtypes = part + [ctypes.POINTER(c_i32), ctypes.POINTER(ctypes.c_double)]
     L.muon_dp_partition.argtypes = part + [ctypes.c_double, ctypes.POINTER(c_i32), ctypes.POINTER(ctypes.c_double)]
     L.muon_mfma_probe.argtypes = [c_vp, c_i32, c_i32, c_vp]
+    L.muon_step_noalloc.argtypes = [ctypes.POINTER(muon_matrix), c_i32, ctypes.POINTER(muon_hparams), c_vp]
     L.muon_tp_micro_groups.argtypes = [ctypes.POINTER(ctypes.c_double), c_i32, c_i32, ctypes.c_double,
                                        ctypes.POINTER(c_i32), ctypes.POINTER(c_i32), ctypes.POINTER(c_i32),
                                        ctypes.POINTER(c_i32)]
@@ -192,6 +194,21 @@ def _descriptors(mats: Iterable[Sequence]):
     if not descs:
         raise MuonError(-1, "empty batch")
     return descs, dtype, tensors
+
+
+def step_noalloc(mats: Iterable[Sequence], stream=None, *, lr=0.02, beta=0.95, eps=1e-7,
+                 coeffs=(3.4445, -4.7750, 2.0315), ns_steps=5, nesterov=True) -> None:
+    """muon_step_noalloc over a batch of ``(W, G, M[, delta])`` device tensors
+    (as for Plan): one step in the library's static scratch, with no plan and
+    no allocation, enqueued on ``stream`` (default: the current stream)."""
+    import torch
+    descs, dtype, _ = _descriptors(mats)
+    hp = make_hparams(lr, beta, eps, coeffs, ns_steps, nesterov, dtype)
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    arr = (muon_matrix * len(descs))(*descs)
+    check(lib().muon_step_noalloc(arr, len(descs), ctypes.byref(hp),
+                                  ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))))
 
 
 class Plan:

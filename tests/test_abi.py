@@ -313,3 +313,40 @@ def test_master_weights_need_the_four_wave_engine(monkeypatch):
     st, out, err = plan_status([desc(0, elem=4)], hp)
     assert st == -4 and "four-wave" in err and out is None
 
+
+# ---- muon_step_noalloc: validation before any HIP call
+
+def noalloc_status(descs, hp=None):
+    hp = hp or muon.make_hparams()
+    arr = (muon.muon_matrix * max(len(descs), 1))(*descs)
+    st = muon.lib().muon_step_noalloc(arr, len(descs), ctypes.byref(hp), None)
+    return st, muon.last_error()
+
+
+def test_noalloc_validates_like_muon_plan():
+    d = [desc(0), desc(1)]
+    d[1].w = d[0].w + 128
+    st, err = noalloc_status(d)
+    assert st == -2 and "overlaps" in err
+    d = [desc(0)]
+    d[0].rows = 0
+    st, err = noalloc_status(d)
+    assert st == -1 and "rows and cols" in err
+    assert muon.lib().muon_step_noalloc(None, 1, None, None) == -1
+
+
+def test_noalloc_rejects_a_workspace_beyond_the_scratch_before_any_hip_call():
+    # 4096 x 4096 bf16 needs about 136 MB of workspace; the scratch holds 64 MiB.
+    d = [desc(0, rows=4096, cols=4096)]
+    d[0].g = d[0].w + (1 << 26)
+    d[0].m = d[0].w + (2 << 26)
+    st, err = noalloc_status(d)
+    assert st == -1 and "static scratch" in err and str(64 << 20) in err
+
+
+def test_no_gpu_noalloc_reports_hip_error_not_crash():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    st, err = noalloc_status([desc(0)])
+    assert st == -5 and err.startswith("hip")
