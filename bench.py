@@ -53,8 +53,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="qwen3_32b_layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", default="1,2,0,3",
-                    help="matrix indices the oracle times for the CPU baseline")
+    ap.add_argument("--cpu-sample", default="all",
+                    help="matrix indices the oracle times for the CPU baseline (comma-separated, or all)")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip the perf-only legs over the other workloads")
     ap.add_argument("--chains", type=int, default=0,
                     help="GEMM chains of the plan (sets MUON_CHAINS; 0: the library default)")
     ap.add_argument("--no-roofline-pass", action="store_true",
@@ -304,6 +306,84 @@ def master_weights_measure(mu, wload, stream, steps, warmup, alg_flops):
             "elementwise_min_bytes_per_elem": 18,
             "what": "the same shapes and step count; the elementwise minimum is 18 B per element "
                     "(read G 2, M 4, W 4; write M' 4, W' 4) against 10 B in bf16"}
+
+
+def other_config_measure(mu, wload, stream, steps=10, runs=2, warmup=3):
+    """A perf-only leg over another workload: the same shapes and dtype with
+    seeded N(0, std^2) data drawn on the GPU (no parity here; the GPU tests
+    compare these workloads with the oracle), `runs` fresh plans of `warmup`
+    untimed and `steps` timed steps each, timed with events on the stream."""
+    import numpy as np
+    import torch
+    dt = torch.bfloat16 if wload.dtype == "bf16" else torch.float32
+    g = torch.Generator(device="cuda").manual_seed(7000 + wload.seed)
+    dev = []
+    for r, c in wload.shapes:
+        W = torch.randn(r, c, device="cuda", generator=g).mul_(wload.w_std).to(dt)
+        G = torch.randn(r, c, device="cuda", generator=g).mul_(wload.g_std).to(dt)
+        M = (torch.randn(r, c, device="cuda", generator=g).mul_(wload.g_std).to(dt)
+             if wload.momentum == "prev" else torch.zeros(r, c, device="cuda", dtype=dt))
+        dev.append([W, G, M])
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(runs):
+        plan = mu.Plan(dev, **wload.hparams())
+        for _ in range(warmup):
+            plan.step(stream)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(steps):
+            plan.step(stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b) / steps)
+        plan.close()
+    del dev
+    torch.cuda.empty_cache()
+    ms = float(np.mean(times))
+    fl = nsflops(wload.shapes, wload.ns_steps)["total"]
+    out = {"matrices": len(wload.shapes), "dtype": wload.dtype, "ms_per_step": round(ms, 4),
+           "ms_per_step_min": round(min(times), 4), "runs": runs, "steps_per_run": steps,
+           "alg_tflop_per_step": round(fl / 1e12, 4)}
+    if wload.dtype == "bf16":
+        tf = fl / (ms / 1e3) / 1e12
+        out.update({"tflops": round(tf, 2), "fraction_of_peak": round(tf / BF16_PEAK_TFLOPS, 4),
+                    "ms_at_half_peak": round(fl / (0.5 * BF16_PEAK_TFLOPS * 1e12) * 1e3, 3)})
+    else:
+        out["note"] = "fp32 and latency-bound (0.0012 TFLOP per step): ms only"
+    return out
+
+
+def hbm_ceiling_measure(stream, mib=2048, reps=10):
+    """What plain streaming kernels reach on this GPU: torch's elementwise
+    copy (read 1, write 1, the momentum kernel's 1:1 mix) and add of two
+    tensors (read 2, write 1, the shard apply's mix) over `mib` MiB per
+    operand of fp32, resident in HBM, timed with events."""
+    import torch
+    n = mib * 2**20 // 4
+    a = torch.empty(n, dtype=torch.float32, device="cuda").uniform_()
+    b = torch.empty_like(a).uniform_()
+    c = torch.empty_like(a)
+    out = {}
+    for name, fn, nbytes in (("copy", lambda: c.copy_(a), 2 * 4 * n),
+                             ("add", lambda: torch.add(a, b, out=c), 3 * 4 * n)):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[name] = {"gbs": round(nbytes / (ms / 1e3) / 1e9, 1), "avg_launch_ms": round(ms, 4),
+                     "bytes_per_launch": nbytes}
+    del a, b, c
+    torch.cuda.empty_cache()
+    out["what"] = (f"torch copy_ and add over {mib} MiB fp32 operands: the streaming rate a plain "
+                   "elementwise kernel reaches, against which the HBM-bound kernels are read")
+    return out
 
 
 def dp_partition_measure(mu, wl, ranks=32, tp=8):
@@ -568,6 +648,13 @@ def main():
     tp_apply = None
     if not args.no_tp_apply:
         tp_apply = aux("tp apply", lambda: tp_apply_measure(mu, wload.shapes, wload.dtype, stream))
+    ceiling = aux("hbm ceiling", lambda: hbm_ceiling_measure(stream))
+    others = None
+    if not args.no_other_configs:
+        others = {}
+        for name, w in wl.WORKLOADS.items():
+            if name != args.workload:
+                others[name] = aux(f"config {name}", lambda w=w: other_config_measure(mu, w, stream))
 
     fl = nsflops(wload.shapes, wload.ns_steps)
     tflops = fl["total"] / (ms_per_step / 1e3) / 1e12
@@ -646,6 +733,8 @@ def main():
         "tp_apply": tp_apply,
         "momentum_hbm": {"achieved_gbs": round(mom_gbs, 1) if mom_gbs else None,
                          "peak_gbs": HBM_PEAK_GBS, "alg_bytes_per_elem": 4 * elem},
+        "hbm_ceiling": ceiling,
+        "other_configs": others,
         "device": torch.cuda.get_device_name(0),
         "host": platform.node(),
     }
@@ -653,8 +742,16 @@ def main():
     del dev
     torch.cuda.empty_cache()
 
+    # The HBM-bound kernels against the streaming ceiling of the same mix.
+    if ceiling and "copy" in ceiling:
+        if mom_gbs:
+            out["momentum_hbm"]["fraction_of_copy_ceiling"] = round(mom_gbs / ceiling["copy"]["gbs"], 4)
+        if tp_apply and tp_apply.get("achieved_gbs"):
+            tp_apply["fraction_of_add_ceiling"] = round(tp_apply["achieved_gbs"] / ceiling["add"]["gbs"], 4)
+
     if not args.no_cpu_baseline:
-        idx = [int(x) for x in args.cpu_sample.split(",") if x != ""]
+        idx = (list(range(len(wload.shapes))) if args.cpu_sample == "all"
+               else [int(x) for x in args.cpu_sample.split(",") if x != ""])
         print(f"[bench] cpu baseline: oracle on matrices {idx}", file=sys.stderr, flush=True)
         try:
             out["cpu_baseline"] = cpu_baseline(wload, idx)

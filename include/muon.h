@@ -227,7 +227,8 @@ typedef struct muon_apply_plan_s* muon_apply_plan_t;
  * initialisation, as the pages' assignment of tensors is. shards is a host
  * array; the plan keeps the device pointers. Every argument is validated
  * before any HIP call. Errors: INVALID_ARG (n < 1, null pointers, rows or
- * cols < 1 or > 2^24, ldp or ldd < cols, more than 2^31 - 1 tiles of 64 x 64),
+ * cols < 1 or > 2^24, ldp or ldd < cols, more than 2^31 - 1 tiles of 16 rows
+ * x 1 KB),
  * ALIGN (p or d not aligned to the element size), ALIAS (an element of a p
  * view is also in another p view or in a d view; d views may share elements),
  * UNSUPPORTED (dtype). Two views with the same row stride are checked element

@@ -810,7 +810,8 @@ muon_status validate_shards(const muon_shard* sh, int32_t n, int32_t dtype) {
     if (s.ldp > (int64_t(1) << 40) || s.ldd > (int64_t(1) << 40)) return fail(MUON_ERR_INVALID_ARG, at + "row stride too large");
     if (reinterpret_cast<uintptr_t>(s.p) % elem || reinterpret_cast<uintptr_t>(s.d) % elem)
       return fail(MUON_ERR_ALIGN, at + "p or d is not aligned to the element size");
-    tiles += ((s.rows + muon::kEwTile - 1) / muon::kEwTile) * ((s.cols + muon::kEwTile - 1) / muon::kEwTile);
+    const int64_t tcols = muon::kApplyRowBytes / int64_t(elem);
+    tiles += ((s.rows + muon::kApplyRows - 1) / muon::kApplyRows) * ((s.cols + tcols - 1) / tcols);
     if (tiles > INT32_MAX) return fail(MUON_ERR_INVALID_ARG, "more than 2^31 - 1 tiles");
     ps.push_back({reinterpret_cast<uintptr_t>(s.p), s.rows, s.cols, s.ldp, i, "p"});
     ds.push_back({reinterpret_cast<uintptr_t>(s.d), s.rows, s.cols, s.ldd, i, "d"});
@@ -860,11 +861,11 @@ muon_status muon_apply_plan(const muon_shard* shards, int32_t n, int32_t dtype, 
     d.ldd = s.ldd;
     d.rows = int32_t(s.rows);
     d.cols = int32_t(s.cols);
-    d.tiles_c = int32_t((s.cols + muon::kEwTile - 1) / muon::kEwTile);
-    const uintptr_t va = 4 * elem;
-    d.vec = s.cols % 4 == 0 && s.ldp % 4 == 0 && s.ldd % 4 == 0 && reinterpret_cast<uintptr_t>(s.p) % va == 0 &&
-            reinterpret_cast<uintptr_t>(s.d) % va == 0;
-    const int32_t tr = int32_t((s.rows + muon::kEwTile - 1) / muon::kEwTile);
+    const int64_t tcols = muon::kApplyRowBytes / int64_t(elem), ve = 16 / int64_t(elem);
+    d.tiles_c = int32_t((s.cols + tcols - 1) / tcols);
+    d.vec = s.cols % ve == 0 && s.ldp % ve == 0 && s.ldd % ve == 0 && reinterpret_cast<uintptr_t>(s.p) % 16 == 0 &&
+            reinterpret_cast<uintptr_t>(s.d) % 16 == 0;
+    const int32_t tr = int32_t((s.rows + muon::kApplyRows - 1) / muon::kApplyRows);
     prefix[i + 1] = prefix[i] + tr * d.tiles_c;
   }
   auto* p = new muon_apply_plan_s();

@@ -12,7 +12,9 @@ namespace muon {
 // epilogue writes 0 outside the valid region.
 constexpr int kTileBF16 = 256;  // bf16 engine: 256 x 256 output tiles, K step 64
 constexpr int kTileF32 = 128;   // fp32 engine: 128 x 128 output tiles, K step 32
-constexpr int kEwTile = 64;     // elementwise kernels: 64 x 64 tiles
+constexpr int kEwTile = 64;     // momentum and apply kernels: 64 x 64 tiles
+constexpr int kApplyRows = 16;  // TP shard apply: 16 rows x 1 KB per workgroup
+constexpr int kApplyRowBytes = 1024;
 
 // GEMM work queues: one per XCD. Persistent workgroup w serves queue
 // w % kQueues first (workgroups are dispatched to the 8 XCDs round-robin), then
@@ -100,14 +102,15 @@ struct EwArgs {
 };
 
 // One view of the TP shard apply (P += D over rows x cols, row strides ldp
-// and ldd). The kernel runs one kEwTile x kEwTile tile per workgroup.
+// and ldd). The kernel runs one tile of kApplyRows rows x kApplyRowBytes
+// bytes per workgroup.
 struct ShardDev {
   void* p;
   const void* d;
   int64_t ldp, ldd;
   int32_t rows, cols;
-  int32_t tiles_c;  // ceil(cols / kEwTile)
-  int32_t vec;      // cols, ldp, ldd multiples of 4 and both pointers 4-element aligned
+  int32_t tiles_c;  // ceil(cols / tile columns), tile columns = kApplyRowBytes / element size
+  int32_t vec;      // cols, ldp, ldd multiples of 16 bytes' worth of elements, both pointers 16-byte aligned
 };
 
 // Launchers (muon_kernels.hip). dtype: 0 = fp32, 1 = bf16.

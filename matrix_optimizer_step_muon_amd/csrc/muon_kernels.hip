@@ -1856,10 +1856,23 @@ MUON_INLINE float block_sum_256(float v, float* red) {
 // Nothing here mixes elements of a tile, except the sum of squares. TG, TM
 // and TX are the storage types of G, of M and of the X buffer (all bf16, all
 // fp32, or bf16 G and X with an fp32 M).
+//
+// A tall matrix's tile goes to X transposed, through LDS. bf16: element
+// (r, c) of the tile is half c % 2 of 4-byte word
+// r * 32 + ((c / 2) ^ (2 * ((r / 4) % 16))). A thread writes its 4 columns as
+// one 8-byte store (the swizzle is even, so the pair of words stays adjacent),
+// and the half-waves of a store cover 2 rows x 32 distinct words; the
+// transposing reads take column c of rows 4k + e, k = 0..15, whose words
+// (c / 2) ^ 2k are 16 distinct even numbers: with the adjacent column's word
+// (the odd one, or the same word read twice) no two lanes meet in one bank
+// at different addresses, for 32- or 64-bank LDS. fp32: rows of 65 floats, so
+// bank (r + c) mod 64 differs across the lanes of both access patterns.
 template <class TG, class TM, class TX>
 __global__ void __launch_bounds__(256) momentum_kernel(EwArgs args) {
   constexpr int TS = kEwTile;
-  __shared__ TX tileU[TS][TS + (sizeof(TX) == 2 ? 2 : 1)];
+  constexpr bool kHalf = sizeof(TX) == 2;
+  __shared__ uint32_t tileW[kHalf ? TS * TS / 2 : 1];
+  __shared__ float tileF[kHalf ? 1 : TS][TS + 1];
   __shared__ float red[4];
   const int tid = threadIdx.x;
   if (blockIdx.x == 0)
@@ -1915,9 +1928,15 @@ __global__ void __launch_bounds__(256) momentum_kernel(EwArgs args) {
       }
     }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      ss += u[e] * u[e];
-      tileU[lr][lc + e] = Elem<TX>::to_storage(u[e]);
+    for (int e = 0; e < 4; ++e) ss += u[e] * u[e];
+    if (tall) {
+      if constexpr (kHalf) {
+        const int w = (lc >> 1) ^ (2 * ((lr >> 2) & 15));
+        *reinterpret_cast<u32x2*>(&tileW[lr * 32 + w]) = u32x2{pack_bf16x2(u[0], u[1]), pack_bf16x2(u[2], u[3])};
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) tileF[lr][lc + e] = u[e];
+      }
     }
   }
   const float tot = block_sum_256(ss, red);  // contains a barrier: tileU is complete
@@ -1931,13 +1950,20 @@ __global__ void __launch_bounds__(256) momentum_kernel(EwArgs args) {
     const int64_t gc = c0 + lc, gr = r0 + lr;
     if (gc >= cols) continue;
     TX* dst = Xb + gc * ldx + gr;
-    if (gr + 3 < rows) {
-      float v[4];
+    float v[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = Elem<TX>::lds_load(&tileU[lr + e][lc]);
+    for (int e = 0; e < 4; ++e) {
+      if constexpr (kHalf) {
+        const uint32_t word = tileW[(lr + e) * 32 + ((lc >> 1) ^ (2 * ((lr >> 2) & 15)))];
+        v[e] = __uint_as_float((lc & 1) ? word & 0xffff0000u : word << 16);
+      } else {
+        v[e] = tileF[lr + e][lc];
+      }
+    }
+    if (gr + 3 < rows) {
       Vec4<TX>::store(dst, v);
     } else {
-      for (int e = 0; e < 4 && gr + e < rows; ++e) Elem<TX>::store(dst + e, Elem<TX>::lds_load(&tileU[lr + e][lc]));
+      for (int e = 0; e < 4 && gr + e < rows; ++e) Elem<TX>::store(dst + e, v[e]);
     }
   }
 }
@@ -1982,39 +2008,61 @@ __global__ void __launch_bounds__(256) apply_kernel(EwArgs args) {
   }
 }
 
-// TP local update: P += D over strided views, one 64 x 64 tile per workgroup
-// of 256 threads (4 rows of 4 elements each). Each sum is formed in fp32 and
-// stored once; for two bf16 (or fp32) values that is their exactly rounded
-// sum.
+// TP local update: P += D over strided views. A workgroup of 4 waves takes
+// kApplyRows rows x 1 KB of one shard: lane l a 16-byte vector of each of the
+// rows wave, wave + 4, ... (8 bf16 or 4 fp32), so every wave instruction
+// moves one contiguous kilobyte of a row. A thread issues all of its P and D
+// loads before its first store. Each sum is formed in fp32 and stored once;
+// for two bf16 (or fp32) values that is their exactly rounded sum.
 template <class T>
 __global__ void __launch_bounds__(256) shard_apply_kernel(const ShardDev* shards, const int32_t* prefix,
                                                           int n) {
-  constexpr int TS = kEwTile;
+  constexpr int VE = 16 / sizeof(T);  // elements per 16-byte vector
+  constexpr int TC = 64 * VE;         // tile columns
+  constexpr int RQ = kApplyRows / 4;  // rows per thread
   const int si = find_mat(prefix, n, blockIdx.x);
   const auto& s = kconst(shards)[si];
   const int local = blockIdx.x - prefix[si];
-  const int64_t r0 = (int64_t)(local / s.tiles_c) * TS;
-  const int64_t c0 = (int64_t)(local % s.tiles_c) * TS;
+  const int64_t r0 = (int64_t)(local / s.tiles_c) * kApplyRows;
+  const int64_t gc = (int64_t)(local % s.tiles_c) * TC + (threadIdx.x & 63) * VE;
+  const int wave = threadIdx.x >> 6;
   T* P = static_cast<T*>(s.p);
   const T* D = static_cast<const T*>(s.d);
-  const int rows = s.rows, cols = s.cols;
-  const int64_t ldp = s.ldp, ldd = s.ldd;
-  const int tid = threadIdx.x;
+  const int64_t rows = s.rows, cols = s.cols, ldp = s.ldp, ldd = s.ldd;
+  if (gc >= cols) return;
+  if (s.vec && gc + VE <= cols) {
+    u32x4 pv[RQ], dv[RQ];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int64_t gr = r0 + q * 16 + (tid >> 4), gc = c0 + (tid & 15) * 4;
-    if (gr >= rows) continue;
-    T* pp = P + gr * ldp + gc;
-    const T* dd = D + gr * ldd + gc;
-    if (s.vec && gc + 3 < cols) {
-      float a[4], b[4];
-      Vec4<T>::load(pp, a);
-      Vec4<T>::load(dd, b);
+    for (int q = 0; q < RQ; ++q) {
+      const int64_t gr = r0 + wave + 4 * q;
+      if (gr < rows) {
+        pv[q] = gload16(P + gr * ldp + gc);
+        dv[q] = gload16(D + gr * ldd + gc);
+      }
+    }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) a[e] += b[e];
-      Vec4<T>::store(pp, a);
-    } else {
-      for (int e = 0; e < 4 && gc + e < cols; ++e) Elem<T>::store(pp + e, Elem<T>::load(pp + e) + Elem<T>::load(dd + e));
+    for (int q = 0; q < RQ; ++q) {
+      const int64_t gr = r0 + wave + 4 * q;
+      if (gr >= rows) continue;
+      u32x4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (sizeof(T) == 2) {
+          o[e] = pack_bf16x2(__uint_as_float(pv[q][e] << 16) + __uint_as_float(dv[q][e] << 16),
+                             __uint_as_float(pv[q][e] & 0xffff0000u) + __uint_as_float(dv[q][e] & 0xffff0000u));
+        } else {
+          o[e] = __float_as_uint(__uint_as_float(pv[q][e]) + __uint_as_float(dv[q][e]));
+        }
+      }
+      *((g_u32x4*)(P + gr * ldp + gc)) = o;
+    }
+  } else {
+    for (int q = 0; q < RQ; ++q) {
+      const int64_t gr = r0 + wave + 4 * q;
+      if (gr >= rows) continue;
+      T* pp = P + gr * ldp + gc;
+      const T* dd = D + gr * ldd + gc;
+      for (int e = 0; e < VE && gc + e < cols; ++e) Elem<T>::store(pp + e, Elem<T>::load(pp + e) + Elem<T>::load(dd + e));
     }
   }
 }
