@@ -172,7 +172,8 @@ typedef enum {
   MUON_K_SQUARE = 3,   /* B = b*A + c*A*A (upper tiles, mirrored)            */
   MUON_K_UPDATE = 4,   /* X = a*X + B X; on the last step, the weight apply  */
   MUON_K_APPLY = 5,    /* weight apply when ns_steps == 0                    */
-  MUON_K_COUNT = 6
+  MUON_K_GRAM_REDUCE = 6, /* sum of split-K Gram pieces, then A's epilogue   */
+  MUON_K_COUNT = 7
 } muon_kernel_kind;
 
 /* enable != 0: every later muon_step records a HIP event pair on its stream

@@ -17,6 +17,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <functional>
 #include <string>
 #include <utility>
 #include <vector>
@@ -97,7 +98,11 @@ struct muon_plan_s {
     int32_t n_tiles[3] = {0, 0, 0};
     int32_t grid[3] = {0, 0, 0};
     int update_variant = muon::kGemm4W;  // engine of this chain's update launches
+    muon::Tile* d_red = nullptr;         // this chain's split Gram tiles (reduce list)
+    int32_t n_red = 0;
   };
+  float* d_kpart = nullptr;  // split-K partial sums of the Gram pieces
+  int32_t split_slots = 0;
   std::vector<Chain> chains;
   std::vector<hipStream_t> aux;
   hipEvent_t ev_fork = nullptr;
@@ -203,9 +208,12 @@ struct PlanTables {
   size_t o_mats = 0, o_prefix = 0, o_cprefix = 0, o_parts = 0, o_scale = 0, o_ctr = 0;
   size_t o_qoff[8] = {};
   size_t o_tiles[8][3] = {};
+  size_t o_red[8] = {};
+  size_t o_kpart = 0;
   std::vector<int32_t> prefix, cprefix;
   std::vector<int32_t> qoff[8];
   std::vector<muon::Tile> tiles[8][3];
+  std::vector<muon::Tile> red[8];
 };
 
 // One host -> device copy of a table into the workspace.
@@ -215,8 +223,96 @@ struct Upload { void* dst; const void* src; size_t bytes; };
 // the workspace layout (p->ws_bytes). No HIP call. one_chain: a single chain
 // whatever the tuning knobs say (the no-allocation step has no second
 // stream). Arguments are validated by the caller.
-muon_status plan_host(const muon_matrix* mats, int32_t n, const muon_hparams* hp, bool one_chain, muon_plan_s* p,
-                      PlanTables& t) {
+// Split-K pieces of each matrix's Gram tiles (1: whole tiles).
+//
+// A Gram launch whose tiles are too few, or too unequal, to keep every CU
+// busy lasts as long as its longest tile: one 1024 x 8192 matrix has 10 Gram
+// tiles of K = 8192 for 256 CUs. Cutting the longest tiles along K into
+// pieces that run on separate CUs, and adding the pieces' partial sums
+// afterwards in a reduce launch, balances the launch. The choice is the
+// pages' LPT reasoning applied to pieces of work (Canzona analysis page,
+// section 3.4, "Why LPT ordering matters"): the planner estimates the
+// launch's makespan with longest-first list scheduling over the CUs, in
+// units of one 64-deep K step, for a few piece counts, and keeps the best if
+// it saves at least 20% (the estimate is rough, and a split that gains
+// little can lose: see below). Only tiles longer than an even share of the work are
+// cut, into pieces of at least 4 K chunks of 256. The costs, measured on
+// MI355X: a whole tile carries its epilogue (about 6 steps); a piece the
+// store of its 256 KB of fp32 partial sums, which all CUs issue at about the
+// same time (about 14 steps); a split the reduce launch (4 steps of launch
+// gap, and its traffic, each piece read and each tile written once, at about
+// 3.5 TB/s). With these, one 1024 x 8192 matrix goes from 1.16 to 0.70 ms per
+// step and two 1024 x 5120 ones from 0.91 to 0.69 ms, while the Qwen3-1.7B
+// layer (where the three MLP matrices' tiles are three times as long as the
+// others, but there are 200 of them) and a 4096 x 16384 matrix (136 tiles of
+// K = 16384) are faster whole, and stay whole. The pieces depend only on the
+// batch's shapes and the CU count, not on the chains or block shapes, so
+// those still change no result. MUON_SPLIT_K=S (a test and tuning knob) cuts
+// every Gram tile into min(S, chunks / 2) pieces instead; S = 1 turns
+// splitting off.
+std::vector<int> gram_pieces(const std::vector<muon::MatDev>& mats, int64_t T, int n_cu) {
+  const int n = int(mats.size());
+  std::vector<int> one(n, 1);
+  std::vector<int64_t> chunks(n), tiles(n);
+  for (int i = 0; i < n; ++i) {
+    chunks[i] = mats[i].np / 256;
+    const int64_t tm = mats[i].mp / T;
+    tiles[i] = tm * (tm + 1) / 2;
+  }
+  if (const char* v = std::getenv("MUON_SPLIT_K")) {
+    const int S = std::max(1, std::min(muon::kMaxSplit, std::atoi(v)));
+    std::vector<int> forced(n);
+    for (int i = 0; i < n; ++i) forced[i] = int(std::max<int64_t>(1, std::min<int64_t>(S, chunks[i] / 2)));
+    return forced;
+  }
+  // Costs in 64-deep K steps (about 1.6 us each on MI355X at its power limit).
+  constexpr double kWhole = 6.0, kPiece = 14.0, kGap = 4.0;
+  constexpr double kReduceBytesPerStep = 3.5e12 * 1.6e-6;
+  constexpr double kPartBytes = 4.0 * muon::kPartFloats;
+  double work = 0.0, longest = 0.0;
+  for (int i = 0; i < n; ++i) {
+    work += double(tiles[i]) * double(chunks[i] * 4);
+    longest = std::max(longest, double(chunks[i] * 4));
+  }
+  if (n_cu < 1) return one;
+  const double share = work / n_cu;
+  if (longest <= share) return one;
+  auto makespan = [&](const std::vector<int>& S) {
+    std::vector<double> items;
+    double reduce_bytes = 0.0;
+    for (int i = 0; i < n; ++i) {
+      for (int p = 0; p < S[i]; ++p) {
+        const int64_t len = (p + 1) * chunks[i] / S[i] - p * chunks[i] / S[i];
+        items.insert(items.end(), size_t(tiles[i]), double(len * 4) + (S[i] > 1 ? kPiece : kWhole));
+      }
+      if (S[i] > 1) reduce_bytes += double(tiles[i]) * (S[i] + 1) * kPartBytes;
+    }
+    std::sort(items.begin(), items.end(), std::greater<double>());
+    std::vector<double> load(size_t(n_cu), 0.0);  // a min-heap of CU loads
+    for (double x : items) {
+      std::pop_heap(load.begin(), load.end(), std::greater<double>());
+      load.back() += x;
+      std::push_heap(load.begin(), load.end(), std::greater<double>());
+    }
+    double span = *std::max_element(load.begin(), load.end());
+    if (reduce_bytes > 0.0) span += kGap + reduce_bytes / kReduceBytesPerStep;
+    return span;
+  };
+  std::vector<int> best = one;
+  const double base = makespan(one);
+  double best_span = base;
+  for (int S : {2, 3, 4, 6, 8, 12, 16}) {
+    std::vector<int> cand(n, 1);
+    for (int i = 0; i < n; ++i)
+      if (double(chunks[i] * 4) > share) cand[i] = int(std::max<int64_t>(1, std::min<int64_t>(S, chunks[i] / 4)));
+    const double span = makespan(cand);
+    if (span < best_span) { best_span = span; best = cand; }
+  }
+  return best_span < 0.8 * base ? best : one;
+}
+
+muon_status plan_host(const muon_matrix* mats, int32_t n, const muon_hparams* hp, bool one_chain, int n_cu,
+                      muon_plan_s* p, PlanTables& t) {
   std::vector<size_t>& off = t.off;
   std::vector<int32_t>& prefix = t.prefix;
   std::vector<int32_t>& cprefix = t.cprefix;
@@ -383,6 +479,24 @@ muon_status plan_host(const muon_matrix* mats, int32_t n, const muon_hparams* hp
         }
   }
   if (const char* v = std::getenv("MUON_BLOCK_ORDER")) border = std::atoi(v) != 0;
+  // Split-K pieces of the Gram tiles (bf16 four-wave engines), their
+  // partial-sum slots (consecutive per tile) and each chain's reduce list.
+  std::vector<int> pieces(n, 1);
+  if (p->gemm_dtype == 1 && four_wave) pieces = gram_pieces(p->mats, T, n_cu);
+  std::vector<int32_t> slot_base(n, 0);
+  int32_t slots = 0;
+  for (int c = 0; c < C; ++c)
+    for (int32_t i = p->chain_first[c]; i < p->chain_first[c + 1]; ++i) {
+      slot_base[i] = slots;
+      if (pieces[i] < 2) continue;
+      const int32_t tm = int32_t(p->mats[i].mp / T);
+      for (int32_t a = 0; a < tm; ++a)
+        for (int32_t cc = a; cc < tm; ++cc) {
+          t.red[c].push_back({i, (a << 16) | cc, pieces[i], slots});
+          slots += pieces[i];
+        }
+    }
+  p->split_slots = slots;
   // Update work (tiles x K) per chain, all of it and that of matrices with at
   // most kSmallTileRows tile rows: see update_variant below.
   int64_t upd_all[8] = {}, upd_small[8] = {};
@@ -396,15 +510,30 @@ muon_status plan_host(const muon_matrix* mats, int32_t n, const muon_hparams* hp
       const int32_t cols = ph == muon::kUpdate ? tn : tm;
       const int64_t K = ph == muon::kGram ? d.np : d.mp;
       const int32_t nbr = (tm + brows - 1) / brows, nbc = (cols + bcols - 1) / bcols;
+      // A split matrix's Gram blocks are formed piece by piece: the tiles of a
+      // block then read the same K range of their panels.
+      const int npc = ph == muon::kGram ? pieces[i] : 1;
+      const int32_t chunks = int32_t(d.np / 256);
+      for (int pc = 0; pc < npc; ++pc)
       for (int32_t bi = 0; bi < nbr * nbc; ++bi) {
         const int32_t r0 = (border ? bi % nbr : bi / nbc) * brows;
         const int32_t c0 = (border ? bi / nbr : bi % nbc) * bcols;
+        const int32_t k0 = pc * chunks / npc, k1 = (pc + 1) * chunks / npc;
         Block b{0, {}};
         for (int32_t a = r0; a < std::min(tm, r0 + brows); ++a)
-          for (int32_t c = c0; c < std::min(cols, c0 + bcols); ++c)
-            if (ph == muon::kUpdate || c >= a) b.tiles.push_back({i, (a << 16) | c});
+          for (int32_t c = c0; c < std::min(cols, c0 + bcols); ++c) {
+            if (!(ph == muon::kUpdate || c >= a)) continue;
+            if (npc == 1) {
+              b.tiles.push_back({i, (a << 16) | c, 0, -1});
+            } else {
+              // Slot of this tile's piece: tiles are numbered row by row over
+              // the upper triangle (the reduce list's order).
+              const int32_t u = a * tm - a * (a - 1) / 2 + (c - a);
+              b.tiles.push_back({i, (a << 16) | c, (k0 << 16) | (k1 - k0), slot_base[i] + u * npc + pc});
+            }
+          }
         if (b.tiles.empty()) continue;
-        b.cost = int64_t(b.tiles.size()) * K;
+        b.cost = int64_t(b.tiles.size()) * (npc == 1 ? K : int64_t(k1 - k0) * 256);
         if (ph == muon::kUpdate) {
           upd_all[c] += b.cost;
           if (tm <= muon::kSmallTileRows) upd_small[c] += b.cost;
@@ -449,8 +578,34 @@ muon_status plan_host(const muon_matrix* mats, int32_t n, const muon_hparams* hp
                                         : p->variant;
     o_tiles[c][ph] = take(sizeof(muon::Tile) * std::max<size_t>(tiles[c][ph].size(), 1));
   }
+  p->chains[c].n_red = int32_t(t.red[c].size());
+  t.o_red[c] = take(sizeof(muon::Tile) * std::max<size_t>(t.red[c].size(), 1));
   }
+  t.o_kpart = take(sizeof(float) * size_t(muon::kPartFloats) * size_t(std::max(slots, 1)));
   p->ws_bytes = cursor;
+  return MUON_OK;
+}
+
+// The engine choice that MUON_GEMM_VARIANT makes, checked against the dtype
+// before any HIP call: fp32 master weights need a four-wave engine.
+muon_status engine_check(const muon_hparams* hp) {
+  if (hp->dtype != MUON_BF16_F32_MASTER) return MUON_OK;
+  if (const char* v = std::getenv("MUON_GEMM_VARIANT")) {
+    const int k = std::atoi(v);
+    if (k == 0 || k == 1)
+      return fail(MUON_ERR_UNSUPPORTED,
+                  "MUON_BF16_F32_MASTER needs the four-wave GEMM engine (MUON_GEMM_VARIANT 2 or 3)");
+  }
+  return MUON_OK;
+}
+
+// Compute units of the current device.
+muon_status device_cus(int* n_cu) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  e = hipDeviceGetAttribute(n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
   return MUON_OK;
 }
 
@@ -491,8 +646,11 @@ std::vector<Upload> plan_bind(muon_plan_s* p, const PlanTables& t, char* base) {
       {p->d_prefix, t.prefix.data(), sizeof(int32_t) * (n + 1)},
       {p->d_cprefix, t.cprefix.data(), sizeof(int32_t) * t.cprefix.size()},
   };
+  p->d_kpart = reinterpret_cast<float*>(base + t.o_kpart);
   for (int c = 0; c < C; ++c) {
     muon_plan_s::Chain& ch = p->chains[c];
+    ch.d_red = reinterpret_cast<muon::Tile*>(base + t.o_red[c]);
+    ups.push_back({ch.d_red, t.red[c].data(), sizeof(muon::Tile) * t.red[c].size()});
     ch.d_qoff = reinterpret_cast<int32_t*>(base + t.o_qoff[c]);
     ups.push_back({ch.d_qoff, t.qoff[c].data(), sizeof(int32_t) * t.qoff[c].size()});
     for (int ph = 0; ph < 3; ++ph) {
@@ -513,9 +671,14 @@ muon_status muon_plan(const muon_matrix* mats, int32_t n, const muon_hparams* hp
   muon_status st = validate(mats, n, hp);
   if (st != MUON_OK) return st;
 
+  st = engine_check(hp);
+  if (st != MUON_OK) return st;
+  int n_cu = 0;
+  st = device_cus(&n_cu);
+  if (st != MUON_OK) return st;
   auto* p = new muon_plan_s();
   PlanTables t;
-  st = plan_host(mats, n, hp, false, p, t);
+  st = plan_host(mats, n, hp, false, n_cu, p, t);
   if (st == MUON_OK) st = plan_device(p);
   if (st != MUON_OK) { free_plan(p); return st; }
   const int C = int(p->chains.size());
@@ -572,6 +735,9 @@ muon_status muon_plan_info(muon_plan_t p, int64_t* n_tiles, int64_t* grid) {
     int64_t t = 0, g = 0;
     if (k == MUON_K_MOMENTUM || k == MUON_K_APPLY) { t = p->ew_blocks; g = p->ew_blocks; }
     else if (k == MUON_K_NORM) { t = p->n; g = p->n; }
+    else if (k == MUON_K_GRAM_REDUCE) {
+      for (const auto& ch : p->chains) { t += ch.n_red; g = std::max<int64_t>(g, ch.n_red); }
+    }
     else {
       for (const auto& ch : p->chains) {
         t += ch.n_tiles[k - MUON_K_GRAM];
@@ -695,12 +861,15 @@ muon_status muon_step(muon_plan_t p, void* stream) {
         hipStream_t q = c == 0 ? s : p->aux[c - 1];
         muon::PhaseArgs a{p->d_mats, ch.d_tiles[ph], ch.d_qoff + ph * (muon::kQueues + 1),
                           p->d_counters + ((c * T + it) * 3 + ph) * muon::kQueues, p->d_scale, it & 1, it == 0,
-                          it == T - 1, p->dtype == MUON_BF16_F32_MASTER ? 1 : 0, co};
+                          it == T - 1, p->dtype == MUON_BF16_F32_MASTER ? 1 : 0, co,
+                          ph == muon::kGram && ch.n_red > 0 ? p->d_kpart : nullptr};
         run_on(q, MUON_K_GRAM + ph,
                [&] {
                  const int v = ph == muon::kUpdate ? ch.update_variant : p->variant;
                  return muon::launch_phase(p->gemm_dtype, v, muon::Phase(ph), a, ch.grid[ph], q);
                });
+        if (ph == muon::kGram && ch.n_red > 0)
+          run_on(q, MUON_K_GRAM_REDUCE, [&] { return muon::launch_gram_reduce(a, ch.d_red, ch.n_red, q); });
       }
     }
   }
@@ -716,14 +885,28 @@ muon_status muon_step(muon_plan_t p, void* stream) {
 
 muon_status muon_step_noalloc(const muon_matrix* mats, int32_t n, const muon_hparams* hp, void* stream) {
   muon_status st = validate(mats, n, hp);
+  if (st == MUON_OK) st = engine_check(hp);
+  if (st != MUON_OK) return st;
+  auto too_big = [](size_t bytes) {
+    return fail(MUON_ERR_INVALID_ARG, "the batch needs " + std::to_string(bytes) + " workspace bytes, more than the " +
+                                          std::to_string(muon::kScratchBytes) + " bytes of static scratch; use muon_plan");
+  };
+  {
+    // Before any HIP call: the workspace without split-K pieces, a lower
+    // bound of the one planned below.
+    muon_plan_s probe;
+    PlanTables t0;
+    st = plan_host(mats, n, hp, true, 0, &probe, t0);
+    if (st == MUON_OK && probe.ws_bytes > muon::kScratchBytes) st = too_big(probe.ws_bytes);
+    if (st != MUON_OK) return st;
+  }
+  int n_cu = 0;
+  st = device_cus(&n_cu);
   if (st != MUON_OK) return st;
   auto* p = new muon_plan_s();
   PlanTables t;
-  st = plan_host(mats, n, hp, true, p, t);
-  if (st == MUON_OK && p->ws_bytes > muon::kScratchBytes)
-    st = fail(MUON_ERR_INVALID_ARG, "the batch needs " + std::to_string(p->ws_bytes) +
-                                        " workspace bytes, more than the " + std::to_string(muon::kScratchBytes) +
-                                        " bytes of static scratch; use muon_plan");
+  st = plan_host(mats, n, hp, true, n_cu, p, t);
+  if (st == MUON_OK && p->ws_bytes > muon::kScratchBytes) st = too_big(p->ws_bytes);
   if (st == MUON_OK) st = plan_device(p);
   void* base = nullptr;
   if (st == MUON_OK) {

@@ -59,11 +59,21 @@ struct MatDev {
   float lr_scale;     // lr * sqrt(max(1, rows / cols))
 };
 
-// One output tile of a GEMM phase: matrix index and tile coordinates.
+// One output tile of a GEMM phase: matrix index and tile coordinates, and
+// for a split-K piece of a Gram tile its K range and partial-sum slot.
 struct Tile {
   int32_t mat;
-  int32_t ij;  // (ti << 16) | tj
+  int32_t ij;    // (ti << 16) | tj
+  int32_t kr;    // 0: the whole K range; else (first 256-wide K chunk << 16) | chunks
+  int32_t slot;  // split-K piece: its fp32 partial-sum slot (kPartFloats floats); -1: none
 };
+
+// A Gram tile split along K runs as pieces, each of which stores its fp32
+// partial sums (one 256 x 256 tile, in the accumulator order of the
+// four-wave engine) in a slot of the plan's split-K buffer; a reduce launch
+// after the Gram launch adds a tile's pieces in piece order and writes A.
+constexpr int kPartFloats = 256 * 256;
+constexpr int kMaxSplit = 16;  // pieces per tile at most
 
 struct StepCoeffs {
   float a, b, c;  // Newton-Schulz polynomial
@@ -88,6 +98,7 @@ struct PhaseArgs {
   int32_t last;        // last iteration: apply to W / delta instead of storing X
   int32_t wf32;        // W and delta are fp32 (fp32 master weights), X, A, B bf16
   StepCoeffs co;
+  float* kpart;        // split-K partial sums (Gram); null when the launch has no pieces
 };
 
 struct EwArgs {
@@ -130,6 +141,9 @@ enum GemmVariant { kGemmBK64 = 0, kGemmBK32 = 1, kGemm4W = 2, kGemm4WDeep = 3 };
 
 hipError_t launch_phase(int dtype, int variant, Phase ph, const PhaseArgs& args, int32_t grid,
                         hipStream_t s);
+// The reduce launch of a chain's split Gram tiles: list[k] = {mat, ij, pieces,
+// first slot} for k < n, one workgroup each (bf16 four-wave engines only).
+hipError_t launch_gram_reduce(const PhaseArgs& args, const Tile* list, int32_t n, hipStream_t s);
 
 // Workgroups per CU that the persistent GEMM kernels can keep resident.
 int gemm_blocks_per_cu(int dtype, int variant);

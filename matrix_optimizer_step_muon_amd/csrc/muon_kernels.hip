@@ -464,7 +464,7 @@ MUON_INLINE const __attribute__((address_space(4))) T* kconst(const T* p) {
 
 MUON_INLINE Tile load_tile(const Tile* tiles, int i) {
   const auto& t = kconst(tiles)[i];
-  return Tile{t.mat, t.ij};
+  return Tile{t.mat, t.ij, t.kr, t.slot};
 }
 
 MUON_INLINE int64_t uniform64(int64_t v) {
@@ -1668,7 +1668,9 @@ MUON_INLINE void apply_half(const unsigned char* epi, const ApplyDev& d, int64_t
 }
 
 // WF32: W and delta are fp32 (fp32 master weights; the last update only).
-template <class E, int PH, bool WF32 = false>
+// KSPLIT: the launch's Gram tiles include split-K pieces (a separate
+// instance, so that the code of launches without pieces stays as it is).
+template <class E, int PH, bool WF32 = false, bool KSPLIT = false>
 __global__ void __launch_bounds__(E::NT) phase_kernel4(PhaseArgs args) {
   static_assert(E::LDS_BYTES + kEpiExtra <= 160 * 1024, "ring + staging exceed LDS");
   static_assert(E::STAGE_BYTES >= kEpiBytes - kEpiExtra, "the staging half must not reach the preloaded stages");
@@ -1715,8 +1717,11 @@ __global__ void __launch_bounds__(E::NT) phase_kernel4(PhaseArgs args) {
     const int64_t tr = (int64_t)ti * E::BM, tc = (int64_t)tj * E::BN;
     Opnd o;
     if constexpr (PH == kGram) {
+      // A split-K piece covers K chunks kr >> 16 .. + (kr & 0xffff) of 256.
       const u16* X = static_cast<const u16*>(d.x[args.src]);
-      o = Opnd{X + tr * d.ldx, d.ldx, X + tc * d.ldx, d.ldx, d.np, 0, 0};
+      const int64_t k0 = (int64_t)(tile.kr >> 16) * 256;
+      const int K = tile.kr ? (tile.kr & 0xffff) * 256 : d.np;
+      o = Opnd{X + tr * d.ldx + k0, d.ldx, X + tc * d.ldx + k0, d.ldx, K, 0, 0};
     } else if constexpr (PH == kSquare) {
       const u16* A = static_cast<const u16*>(d.a);
       const int dg = f.sq_mode == 2;
@@ -1771,7 +1776,22 @@ __global__ void __launch_bounds__(E::NT) phase_kernel4(PhaseArgs args) {
     const float s = kconst(args.scale)[tile.mat];
     // Each half: stage, barrier, read out, barrier (the second half's closing
     // barrier is the next tile's first one when it was preloaded).
-    if constexpr (PH == kGram || PH == kSquare) {
+    if (KSPLIT && PH == kGram && tile.slot >= 0) {
+      // A split-K piece: its partial sums go to its slot in accumulator
+      // order (thread t's 16 values of block (i, j) at 16 * (256 (4i + j) +
+      // t)), so every wave stores 4 KB contiguous per block and the reduce
+      // launch reads them back in the same layout. No LDS is touched.
+      float* dst = args.kpart + (int64_t)tile.slot * kPartFloats + 16 * (int)threadIdx.x;
+#pragma unroll
+      for (int i = 0; i < E::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < E::FN; ++j)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const f32x4 x = {acc[i][j][4 * v], acc[i][j][4 * v + 1], acc[i][j][4 * v + 2], acc[i][j][4 * v + 3]};
+            *((g_f32x4*)(dst + 4096 * (i * E::FN + j) + 4 * v)) = x;
+          }
+    } else if constexpr (PH == kGram || PH == kSquare) {
       // gram: A' = g s^2 U U^T on the first iteration (X holds U), else g X X^T.
       // square: B'' = sq * (A' A' + A') + I (the update's identity term; only
       //   when the update has it, and only a diagonal tile has a diagonal).
@@ -1829,6 +1849,77 @@ __global__ void __launch_bounds__(E::NT) phase_kernel4(PhaseArgs args) {
       oc = operands(cur);
       pre = false;
     }
+  }
+}
+
+// Sum of a split Gram tile's pieces, then the Gram epilogue: A' = g (s^2)
+// X X^T for the tile and its mirror. Four workgroups per tile, one per
+// 128 x 128 quadrant (the sub-tile one wave of the four-wave engine held).
+// In the pieces' layout, quadrant w's 16 accumulator blocks (i, j) are 4 KB
+// each: lane l's 16 values at 16 (256 (4i + j) + 64 w + l). Here wave v takes
+// block row i = v: lane l holds quadrant row 32v + l % 32 and, for each j, the
+// 16 columns 32j + 8g + 4(l / 32) + q (g, q < 4) of it. The sums (in piece
+// order), scaled, go to a bf16 staging tile of 128 rows (pitch 136 elements,
+// so that 8 consecutive rows of one column fall in 8 different banks), which
+// is written out by rows (16 bytes per lane) and, for an off-diagonal tile,
+// by columns to the mirror (8 rows gathered per 16-byte store). Entries
+// outside the matrix are written as 0, as the Gram kernel's are.
+__global__ void __launch_bounds__(256) gram_reduce_kernel(PhaseArgs args, const Tile* list) {
+  constexpr int QP = 136;  // staging pitch in bf16 elements
+  __shared__ __attribute__((aligned(16))) u16 stage[128 * QP];
+  const Tile tile = load_tile(list, blockIdx.x >> 2);
+  const int w = blockIdx.x & 3, wm = w >> 1, wn = w & 1;
+  const auto& d = kconst(args.mats)[tile.mat];
+  const int ti = tile.ij >> 16, tj = tile.ij & 0xffff, pieces = tile.kr;
+  const int tid = threadIdx.x, lane = tid & 63, v = tid >> 6;
+  const float s = kconst(args.scale)[tile.mat];
+  const float sc = (args.first ? s * s : 1.f) * fold_coeffs(args.co).g;
+  // Valid rows and columns of this quadrant (the tile is m x m at most).
+  const int64_t qr = (int64_t)ti * 256 + wm * 128, qc = (int64_t)tj * 256 + wn * 128;
+  const int rl = (int)(d.m - qr < 128 ? (d.m - qr > 0 ? d.m - qr : 0) : 128);
+  const int cl = (int)(d.m - qc < 128 ? (d.m - qc > 0 ? d.m - qc : 0) : 128);
+  const int row = 32 * v + (lane & 31);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float* src = args.kpart + (int64_t)tile.slot * kPartFloats + 16 * (256 * (4 * v + j) + 64 * w + lane);
+    f32x4 x[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) x[g] = *((const g_f32x4*)(src + 4 * g));
+    for (int pc = 1; pc < pieces; ++pc) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 y = *((const g_f32x4*)(src + (int64_t)pc * kPartFloats + 4 * g));
+        x[g][0] += y[0]; x[g][1] += y[1]; x[g][2] += y[2]; x[g][3] += y[3];
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int col = 32 * j + 8 * g + 4 * (lane >> 5);
+      float o[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) o[q] = (row < rl && col + q < cl) ? sc * x[g][q] : 0.f;
+      *reinterpret_cast<u32x2*>(&stage[row * QP + col]) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+    }
+  }
+  __syncthreads();
+  u16* A = static_cast<u16*>(d.a);
+  // Rows: 128 rows x 256 bytes, 16 lanes per row.
+#pragma unroll 4
+  for (int p = 0; p < 8; ++p) {
+    const int idx = tid + 256 * p, r = idx >> 4, c8 = (idx & 15) * 8;
+    *((g_u32x4*)(A + (qr + r) * d.lda + qc + c8)) = *reinterpret_cast<const u32x4*>(&stage[r * QP + c8]);
+  }
+  if (ti == tj) return;
+  // Mirror: row c of the mirror quadrant gets column c of the staging tile;
+  // a lane gathers 8 consecutive staged rows of one column.
+#pragma unroll 4
+  for (int p = 0; p < 8; ++p) {
+    const int idx = tid + 256 * p, c = idx & 127, r8 = (idx >> 7) * 8;
+    u32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      o[e] = (uint32_t)stage[(r8 + 2 * e) * QP + c] | ((uint32_t)stage[(r8 + 2 * e + 1) * QP + c] << 16);
+    *((g_u32x4*)(A + (qc + c) * d.lda + qr + r8)) = o;
   }
 }
 
@@ -2235,7 +2326,10 @@ static hipError_t launch_phase_e(Phase ph, const PhaseArgs& args, int32_t grid, 
 template <class E, class EQ>
 static hipError_t launch_phase_e4(Phase ph, const PhaseArgs& args, int32_t grid, hipStream_t s) {
   switch (ph) {
-    case kGram: hipLaunchKernelGGL((phase_kernel4<E, kGram>), dim3(grid), dim3(E::NT), 0, s, args); break;
+    case kGram:
+      if (args.kpart) hipLaunchKernelGGL((phase_kernel4<E, kGram, false, true>), dim3(grid), dim3(E::NT), 0, s, args);
+      else hipLaunchKernelGGL((phase_kernel4<E, kGram>), dim3(grid), dim3(E::NT), 0, s, args);
+      break;
     case kSquare: hipLaunchKernelGGL((phase_kernel4<E, kSquare>), dim3(grid), dim3(E::NT), 0, s, args); break;
     default:
       if (args.last && args.wf32)
@@ -2255,6 +2349,12 @@ hipError_t launch_phase(int dtype, int variant, Phase ph, const PhaseArgs& args,
   if (variant == kGemm4W) return launch_phase_e4<Engine4<false, 64, 2>, Engine4<true, 64, 2>>(ph, args, grid, s);
   if (variant == kGemm4WDeep) return launch_phase_e4<Engine4<false, 32, 4>, Engine4<true, 32, 4>>(ph, args, grid, s);
   return launch_phase_e<EngineBF16<2, 4, 64, 2, false>, EngineBF16<2, 4, 64, 2, true>>(ph, args, grid, s);
+}
+
+hipError_t launch_gram_reduce(const PhaseArgs& args, const Tile* list, int32_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(gram_reduce_kernel, dim3(4 * n), dim3(256), 0, s, args, list);
+  return hipGetLastError();
 }
 
 int gemm_blocks_per_cu(int dtype, int variant) {

@@ -18,7 +18,7 @@ MUON_OK = 0
 STATUS_NAMES = {0: "OK", -1: "INVALID_ARG", -2: "ALIAS", -3: "ALIGN", -4: "UNSUPPORTED",
                 -5: "HIP", -6: "OOM"}
 MUON_F32, MUON_BF16, MUON_BF16_F32_MASTER = 0, 1, 2
-KERNEL_KINDS = ("momentum", "norm", "gram", "square", "update", "apply")
+KERNEL_KINDS = ("momentum", "norm", "gram", "square", "update", "apply", "gram_reduce")
 MUON_K_COUNT = len(KERNEL_KINDS)
 
 

@@ -71,8 +71,8 @@ def test_default_engine_k_loops_do_not_spill(kernel_asm):
     # Engine4<QK, 64, 2>: K step 64 = 4 sub-steps of 16 MFMAs.
     loops = _k_step_loops(kernel_asm, r"phase_kernel4INS_7Engine4ILb[01]ELi64ELi2EEE", 64)
     kernels = {k for k, _, _, _ in loops}
-    assert len(kernels) == 5, ("expected the gram, square, update and last-update kernels (bf16 and fp32 W), "
-                               f"found {kernels}")
+    assert len(kernels) == 6, ("expected the gram (with and without split-K pieces), square, update and "
+                               f"last-update kernels (bf16 and fp32 W), found {kernels}")
     bad = [(k[-40:], n, s) for k, n, _, s in loops if s]
     assert not bad, f"K-step loops with scratch accesses (kernel, length, accesses): {bad}"
 

@@ -82,6 +82,45 @@ def test_other_polynomial_coefficients(dtype, coeffs):
     compare(gpu, want, dtype, hp, inputs, f"coeffs={coeffs} {dtype}")
 
 
+SPLIT_SHAPES = [(1000, 3000), (3000, 1000), (300, 2300), (129, 1030), (1, 5), (512, 4096)]
+
+
+def _with_env(env, fn):
+    import os
+    saved = {k: os.environ.get(k) for k in env}
+    os.environ.update({k: str(v) for k, v in env.items()})
+    try:
+        return fn()
+    finally:
+        for k, v in saved.items():
+            if v is None:
+                del os.environ[k]
+            else:
+                os.environ[k] = v
+
+
+@pytest.mark.parametrize("split", [2, 3, 5])
+def test_split_k_gram_pieces(split):
+    """MUON_SPLIT_K=S cuts every Gram tile into min(S, K/512) pieces along K
+    (uneven ones too: 9 chunks of 256 in 4 pieces, say), whose fp32 partial
+    sums a reduce launch adds in piece order. The step still meets the bar
+    against the oracle, it is deterministic, and one and two chains (the
+    pieces of a matrix do not depend on the chains) agree bit for bit."""
+    w = wl.custom_workload(f"split{split}", SPLIT_SHAPES, "bf16", seed=23)
+    inputs = wl.generate(w)
+    hp = w.hparams()
+    log(f"case split-K {split}")
+    got = _with_env({"MUON_SPLIT_K": split}, lambda: gpu_step(inputs, "bf16", hp, steps=2))
+    want = oracle_step(inputs, "bf16", hp, steps=2)
+    compare(got, want, "bf16", hp, inputs, f"split-K {split}")
+    again = _with_env({"MUON_SPLIT_K": split}, lambda: gpu_step(inputs, "bf16", hp, steps=2))
+    one = _with_env({"MUON_SPLIT_K": split, "MUON_CHAINS": 1}, lambda: gpu_step(inputs, "bf16", hp, steps=2))
+    for i in range(len(SPLIT_SHAPES)):
+        for name, x, y, z in zip(("W'", "M'", "delta"), got[i], again[i], one[i]):
+            assert np.array_equal(x, y), f"matrix {i}: {name} differs between two split runs"
+            assert np.array_equal(x, z), f"matrix {i}: {name} differs between one and two chains"
+
+
 def test_bf16_stores_round_to_nearest_even():
     """M' = beta*M + G is formed in fp32 and stored once as bf16. Every stored
     value must be the nearest-even bf16 of the fp32 value, whether the fp32
