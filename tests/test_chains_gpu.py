@@ -21,6 +21,9 @@ pytestmark = pytest.mark.gpu
 
 # Several matrices of different work, so that both chains get some.
 SHAPES = [(1024, 768), (768, 1536), (512, 512), (1280, 256), (300, 700), (256, 2048)]
+# The schedule test adds a matrix with m in (2048, 4096] (8 x 8 blocks and the
+# 4-stage update engine by default).
+SCHEDULE_SHAPES = SHAPES + [(2560, 3072)]
 
 
 def _with_env(name, value, fn):
@@ -90,7 +93,7 @@ def test_tile_schedule_does_not_change_results(env):
     update launches: these shapes (m <= 4096) update on the 4-stage engine by
     default, and MUON_GEMM_VARIANT=2 puts them on the 2-stage one, which sums
     the same K chunks in the same order."""
-    w = wl.custom_workload("schedule", SHAPES, "bf16", seed=57)
+    w = wl.custom_workload("schedule", SCHEDULE_SHAPES, "bf16", seed=57)
     inputs = wl.generate(w)
     hp = w.hparams()
     log(f"case tile schedule {env}")
@@ -105,4 +108,4 @@ def test_tile_schedule_does_not_change_results(env):
     got = fn()
     for i, (a, b) in enumerate(zip(ref_out, got)):
         for name, x, y in zip(("W'", "M'", "delta"), a, b):
-            assert np.array_equal(x, y), f"matrix {i} {SHAPES[i]}: {name} differs under {env}"
+            assert np.array_equal(x, y), f"matrix {i} {SCHEDULE_SHAPES[i]}: {name} differs under {env}"
