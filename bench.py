@@ -716,7 +716,9 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(upd_tflops / peak, 4) if upd_tflops else None,
             "traffic": committed_traffic(args.workload),
-            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-scaled)",
+            "traffic_unit": ("bytes per launch at the L2's memory-side interface (rocprofv3 FETCH_SIZE + "
+                             "WRITE_SIZE, copy-scaled): L2 misses, all addressed to DRAM; the Infinity Cache's "
+                             "share of them has no counter on this GPU"),
             "alg_tflop_per_launch": round(upd_flops / 1e12, 4),
             "launches_per_step": upd_per_step,
             "timed_in": "a separate single-chain pass of the same steps",
