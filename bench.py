@@ -511,7 +511,7 @@ def committed_traffic(workload: str):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(the Muon step of one rank needs no communication, so N ranks run N independent "
               "copies of this benchmark)", file=sys.stderr)
         sys.exit(2)

@@ -452,7 +452,7 @@ muon_status plan_host(const muon_matrix* mats, int32_t n, const muon_hparams* hp
   // knobs: MUON_BLOCK=RxC sets the block shape in tiles, and
   // MUON_BLOCK_ORDER=0 walks blocks row-major instead.
   // 4 x 4 blocks: 1.2% less step time than 4 x 8 on the Qwen3-32B layer with
-  // two chains, 0.9% with one (same box; 2 x 8, 4 x 2, 2 x 4, 3 x 4, 4 x 3,
+  // two chains, 0.9% with one (same GPU; 2 x 8, 4 x 2, 2 x 4, 3 x 4, 4 x 3,
   // 4 x 6, 6 x 4 and 8 x 4 are all slower than 4 x 4).
   // bf16 matrices of at most kSmallTileRows tile rows take kSmallBlock x
   // kSmallBlock blocks (small_blocks); MUON_BLOCK or MUON_BLOCK_PHASES set one

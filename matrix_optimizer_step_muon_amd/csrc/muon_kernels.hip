@@ -545,7 +545,7 @@ struct Engine4 {
   static constexpr int SLOT_NUM = 7, SLOT_DEN = 4;  // 2-stage ring: load d at MFMA d * 7 / 4
   // The wait for step kt+1 and the barrier come after SPLIT of the last
   // sub-step's 16 MFMAs; the other 16 - SPLIT MFMAs cover the first fragment
-  // reads of step kt+1. Measured (step time, same box): SPLIT 8 and 10 cost
+  // reads of step kt+1. Measured (step time, same GPU): SPLIT 8 and 10 cost
   // 0.4% and 0.5% more than 12 to 15; the update does best at 12, gram at 14.
   static constexpr int SPLIT = QK ? 12 : 14;
   static constexpr int WAIT_AT = (KK - 1) * 16 + SPLIT;  // MFMAs of a step issued before its wait

@@ -22,7 +22,7 @@ def _gpu_visible() -> bool:
 
 
 def pytest_collection_modifyitems(config, items):
-    # GPU tests are skipped only when no GPU is visible at all. On a GPU machine a
+    # GPU tests are skipped only when no GPU is visible at all. With a GPU, a
     # missing or broken library makes them fail, never fall back.
     if any("gpu" in item.keywords for item in items) and not _gpu_visible():
         skip = pytest.mark.skip(reason="no GPU visible")
